@@ -1,0 +1,160 @@
+/*
+ * ra.h -- C ABI of the ring-attention share library for AMD MI355X (gfx950).
+ *
+ * The method (slowleelab "Ring Attention" page, L3 definition and L4 section 4.2):
+ * a sequence of L tokens is split into N equal blocks of l = L / N tokens; ring
+ * member i keeps its query block Q_i resident and, at step t = 0 .. N-1, works on
+ * the K/V block (i - t) mod N, which arrives from member i-1 and is passed on to
+ * member i+1.  Each step is one blockwise, FlashAttention-style merge with online
+ * softmax (same page, 4.3): a running row maximum m, a running sum l of
+ * exp(s - m) and an unnormalised output O are rescaled and accumulated per block,
+ * and O is divided by l once after the last block.  After the N steps, Q_i's
+ * output is exact attention softmax(Q_i K^T / sqrt(d)) V over the whole sequence.
+ * On one GPU the arrival of blocks over the ring is replaced by a rotating index
+ * over K/V blocks that are already resident in device memory.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory and keeps no state between calls, except a
+ *    per-device record of whether the device is supported.
+ *  - Layouts are row-major: Q_i and outputs O are [B, H, l_q, d]; K and V are
+ *    [B, H_kv, rows, d]; m and l are fp32 [B, H, l_q]; O_acc is always fp32.
+ *  - Grouped-query attention (lnwmold page, section 2.2): query head h reads K/V
+ *    head h / (H / H_kv); H must be a multiple of H_kv.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *    compute call only enqueues work on that stream and returns; errors inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - Return value: RA_OK, or an ra_status code.  Arguments are validated before
+ *    anything is enqueued, so an RA_EINVAL / RA_ENOTSUP return means no device
+ *    memory was written.  Input VALUES are not checked: NaN and Inf propagate.
+ *  - Supported: d in {64, 128}; dtype RA_F32 or RA_BF16; scale finite and > 0;
+ *    device pointers 16-byte aligned.  Any N >= 1 is allowed (the slowleelab page,
+ *    pitfall 6, notes the ring works for any GPU count).
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ra_status {
+    RA_OK = 0,
+    RA_EINVAL = 1,  /* bad argument; nothing was enqueued */
+    RA_ENOTSUP = 2, /* current device is not gfx950, or an unsupported size */
+    RA_EHIP = 3     /* a HIP runtime call failed; see ra_last_hip_error() */
+} ra_status;
+
+typedef enum ra_dtype {
+    RA_F32 = 0,  /* fp32 Q/K/V; fp32 arithmetic throughout */
+    RA_BF16 = 1  /* bf16 Q/K/V; bf16 matrix-core products, fp32 accumulation and statistics */
+} ra_dtype;
+
+/*
+ * Shape of one step's operands.
+ *   B, H, H_kv, d   batch, query heads, K/V heads, head dimension
+ *   l_q             rows of the resident query block Q_i
+ *   l_kv            rows (keys) of the K/V block merged by this step
+ *   kv_head_stride  elements between consecutive K/V heads of K_blk / V_blk;
+ *                   0 means l_kv * d (a contiguous [B, H_kv, l_kv, d] block, as
+ *                   received over a ring); L * d addresses a block inside a full
+ *                   [B, H_kv, L, d] tensor.  Must be a multiple of 8.
+ *   kv_batch_stride elements between batches of K_blk / V_blk; 0 means
+ *                   H_kv * kv_head_stride.  Must be a multiple of 8.
+ *   dtype           an ra_dtype for Q_i, K_blk and V_blk
+ */
+typedef struct ra_shape {
+    int32_t B, H, H_kv, d;
+    int64_t l_q, l_kv;
+    int64_t kv_head_stride, kv_batch_stride;
+    int32_t dtype;
+} ra_shape;
+
+/*
+ * K/V block that ring member `rank` uses at step t: (rank - t) mod N, always in
+ * [0, N).  slowleelab page, L3 ("at step t GPU i receives K_(i-t)%N, V_(i-t)%N
+ * from GPU i-1 ... then sends it to GPU i+1") and the N = 4 table in 4.2.
+ * Host only.  Returns -RA_EINVAL if N < 1, rank outside [0, N) or t outside [0, N).
+ */
+int32_t ra_ring_block(int32_t rank, int32_t N, int32_t t);
+
+/*
+ * Fills host array out[0 .. N-1] with ra_ring_block(rank, N, t).  Host only.
+ * Returns RA_EINVAL (and writes nothing) on bad rank / N or a NULL `out`.
+ */
+int ra_ring_schedule(int32_t rank, int32_t N, int32_t *out);
+
+/*
+ * K/V head read by query head h under grouped-query attention with contiguous
+ * groups of H / H_kv heads (lnwmold page, sections 2.2 and 3.1).  Host only.
+ * Returns -RA_EINVAL if H % H_kv != 0 or h is outside [0, H).
+ */
+int32_t ra_kv_head(int32_t h, int32_t H, int32_t H_kv);
+
+/*
+ * Initial running state before the first step: O_acc = 0, m = -inf, l = 0.
+ * (The slowleelab page's step pseudocode, 4.3, leaves the initial state
+ * unstated; this is the state for which merging one block gives that block's
+ * own attention.)  O_acc is [B, H, l_q, d] fp32; m and l are [B, H, l_q] fp32.
+ * Uses shape fields B, H, d, l_q.  l_q == 0 is a no-op.
+ */
+int ra_state_init(float *O_acc, float *m, float *l, const ra_shape *s, void *stream);
+
+/*
+ * One ring step: merges the K/V block (K_blk, V_blk) into the running state of
+ * the resident block Q_i, in place (slowleelab page, 4.3, ring_attention_step):
+ *     s      = scale * Q_i K_blk^T                (per query row, per key)
+ *     m_new  = max(m, row max of s)
+ *     l     <- exp(m - m_new) * l + row sum of exp(s - m_new)
+ *     O_acc <- exp(m - m_new) * O_acc + exp(s - m_new) V_blk
+ *     m     <- m_new
+ * Division by l is NOT done here (it is the final rescale, ra_finalize).  After
+ * the call, m is exactly the running row maximum of the fp32 scores seen so far.
+ * Blocks may be merged in any order; the finalised result does not depend on it.
+ * Q_i is [B, H, l_q, d] contiguous; K_blk / V_blk are [B, H_kv, l_kv, d] with the
+ * strides in *s.  l_q == 0 or l_kv == 0 is a no-op.  scale is normally 1/sqrt(d).
+ */
+int ra_step(const void *Q_i, const void *K_blk, const void *V_blk, float *O_acc,
+            float *m, float *l, float scale, const ra_shape *s, void *stream);
+
+/*
+ * Final rescale after the last step (slowleelab page, 4.3, "O_i / l_new"):
+ * O_acc <- O_acc / l per row, in place.  If O_out is not NULL it also receives the
+ * result in s->dtype (bf16 rounded to nearest even, or an fp32 copy).  Uses shape
+ * fields B, H, d, l_q, dtype.  Defined only after at least one step (l > 0).
+ */
+int ra_finalize(float *O_acc, const float *l, const ra_shape *s, void *O_out, void *stream);
+
+/*
+ * The whole share of ring member `rank` in one launch: all N blocks of the
+ * sequence, visited in the order ra_ring_schedule(rank, N), merged with online
+ * softmax and finalised.
+ *   L          sequence length; must be a multiple of N; l = L / N
+ *   Q_i        [B, H, l, d] in `dtype`, the resident query block
+ *   K, V       [B, H_kv, L, d] in `dtype`, the full sequence; block j is rows
+ *              j*l .. (j+1)*l - 1
+ *   O          [B, H, l, d] fp32, the finalised attention output (required)
+ *   m_out      nullable [B, H, l] fp32: row maximum of the scaled scores
+ *   l_out      nullable [B, H, l] fp32: sum over all keys of exp(s - m_out)
+ *   O_cast     nullable [B, H, l, d] in `dtype` (bf16 rounded to nearest even)
+ *   sched_trace nullable device int32[N]: the block index used at each step t
+ * L == 0 is a no-op.
+ */
+int ra_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                     int32_t d, int32_t B, int32_t dtype, const void *Q_i, const void *K,
+                     const void *V, float scale, float *O, float *m_out, float *l_out,
+                     void *O_cast, int32_t *sched_trace, void *stream);
+
+/* Static description of a status code. */
+const char *ra_strerror(int status);
+
+/* The hipError_t of the last failing HIP call on this thread (0 if none). */
+int ra_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -1,0 +1,194 @@
+"""Plain fp64 CPU oracle for one ring member's attention share.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this package.  The product path (the HIP library and
+its Python binding) never imports, loads or calls anything here, and this package
+imports nothing from the product path.
+
+Contents
+--------
+ring_schedule(rank, N)
+    The ring visiting order: at step t, rank i works on K/V block (i - t) mod N
+    (slowleelab "Ring Attention" page, L3 definition and the 4.2 algorithm).
+kv_head(h, H, H_kv)
+    Grouped-query head sharing, contiguous groups (lnwmold page, section 2.2).
+attention_rows(...)
+    The plain definition softmax(Q K^T * scale) V over a set of key ranges, fp64,
+    every score materialised (C code in ra_oracle.c).  Returns the normalised
+    output together with the row maximum M and the sum Z of exp(s - M).
+online_step(...)
+    One merge of a K/V block into the running state (O_acc, m, l), in the order of
+    the per-step pseudocode on the slowleelab page (section 4.3), fp64 numpy, with
+    the readings listed in the design notes (row-wise max, exp(S - m_new) in both
+    the sum and the output, division deferred to the final rescale, initial state
+    O = 0, m = -inf, l = 0).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ra_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libra_oracle.so")
+_lib = None
+
+F32 = 0
+BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile ra_oracle.c with gcc (fp64, OpenMP) into oracle/libra_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.ra_oracle_rows.restype = ctypes.c_int
+        lib.ra_oracle_rows.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64, i64p, i64p,
+            ctypes.c_int, f64p, f64p, f64p, ctypes.c_int]
+        lib.ra_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().ra_oracle_max_threads())
+
+
+def ring_schedule(rank: int, N: int) -> list[int]:
+    """K/V block used by `rank` at steps t = 0..N-1: (rank - t) mod N.
+
+    slowleelab page, L3: at step t GPU i receives K/V block (i-t)%N from GPU i-1 and
+    passes it on to GPU i+1; the N=4 table in 4.2 shows step 0 using the local block.
+    Python's % already yields the non-negative remainder.
+    """
+    if N < 1 or not 0 <= rank < N:
+        raise ValueError("need N >= 1 and 0 <= rank < N")
+    return [(rank - t) % N for t in range(N)]
+
+
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """K/V head shared by query head h: contiguous groups of H/H_kv query heads."""
+    if H % H_kv != 0 or not 0 <= h < H:
+        raise ValueError("need H % H_kv == 0 and 0 <= h < H")
+    return h // (H // H_kv)
+
+
+def _raw(a: np.ndarray):
+    """(dtype code, contiguous buffer) of an fp32 array or a bf16-bits uint16 array."""
+    if a.dtype == np.float32:
+        return F32, np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return BF16, np.ascontiguousarray(a)
+    raise TypeError("inputs must be float32 arrays or uint16 arrays holding bf16 bits")
+
+
+def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                   rows=None, key_ranges=None, nthreads: int | None = None):
+    """The plain definition over the listed key ranges, for the listed query rows.
+
+    Q: [B, H, l_q, d]; K, V: [B, H_kv, L, d]; all float32, or all uint16 bf16 bits.
+    rows: flat indices (b*H + h)*l_q + r (default: every row).
+    key_ranges: list of (lo, hi) half-open key ranges (default: all L keys).
+    scale: the fp32 scale the GPU uses, widened to fp64 here.
+    Returns (O [n, d] float64 normalised, M [n] float64, Z [n] float64).
+    """
+    dq, Qb = _raw(Q)
+    dk, Kb = _raw(K)
+    dv, Vb = _raw(V)
+    if not dq == dk == dv:
+        raise TypeError("Q, K and V must share a dtype")
+    B, H, l_q, d = Qb.shape
+    Bk, H_kv, L, dk_ = Kb.shape
+    if Vb.shape != Kb.shape or Bk != B or dk_ != d:
+        raise ValueError("shape mismatch")
+    if rows is None:
+        rows = np.arange(B * H * l_q, dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if key_ranges is None:
+        key_ranges = [(0, L)]
+    lo = np.ascontiguousarray(np.array([r[0] for r in key_ranges], dtype=np.int64))
+    hi = np.ascontiguousarray(np.array([r[1] for r in key_ranges], dtype=np.int64))
+    n = rows.shape[0]
+    O = np.empty((n, d), dtype=np.float64)
+    M = np.empty((n,), dtype=np.float64)
+    Z = np.empty((n,), dtype=np.float64)
+    if nthreads is None:
+        nthreads = max_threads()
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    rc = _load().ra_oracle_rows(
+        dq, Qb.ctypes.data, l_q, Kb.ctypes.data, Vb.ctypes.data, L, B, H, H_kv, d,
+        float(scale), rows.ctypes.data_as(i64p), n, lo.ctypes.data_as(i64p),
+        hi.ctypes.data_as(i64p), len(key_ranges), O.ctypes.data_as(f64p),
+        M.ctypes.data_as(f64p), Z.ctypes.data_as(f64p), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"ra_oracle_rows failed with code {rc}")
+    return O, M, Z
+
+
+def share(Q, K, V, scale, rank: int, N: int, rows=None, steps: int | None = None,
+          nthreads=None):
+    """Rank `rank`'s share after `steps` ring steps (default all N): the definition
+    restricted to the keys of blocks ring_schedule(rank, N)[:steps]."""
+    L = K.shape[2]
+    if L % N != 0:
+        raise ValueError("L must split evenly into N blocks")
+    l = L // N
+    order = ring_schedule(rank, N)[: (N if steps is None else steps)]
+    ranges = [(j * l, (j + 1) * l) for j in order]
+    return attention_rows(Q, K, V, scale, rows=rows, key_ranges=ranges, nthreads=nthreads)
+
+
+def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def init_state(rows: int, d: int):
+    """Initial running state: O = 0, m = -inf, l = 0 (the pages leave it unstated)."""
+    return (np.zeros((rows, d)), np.full((rows,), -np.inf), np.zeros((rows,)))
+
+
+def online_step(state, q: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray, scale: float):
+    """Merge one K/V block into (O_acc, m, l), fp64, rows independent.
+
+    q: [R, d]; k_blk, v_blk: [n, d] (fp64).  Follows the slowleelab page's per-step
+    pseudocode (section 4.3): block scores, new running maximum, rescale of the old sum
+    and old output by exp(m - m_new), accumulation of the block's exponentials.  The
+    maximum is taken per row, the exponentials are taken relative to m_new, and no
+    division happens here (it is the final rescale, see finalize()).
+    """
+    O, m, l = state
+    S = (q @ k_blk.T) * scale                      # [R, n]
+    m_new = np.maximum(m, S.max(axis=1))
+    alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
+    P = np.exp(S - m_new[:, None])
+    l_new = alpha * l + P.sum(axis=1)
+    O_new = alpha[:, None] * O + P @ v_blk
+    return O_new, m_new, l_new
+
+
+def finalize(state):
+    """The final rescale O / l, applied once after the last step."""
+    O, m, l = state
+    return O / l[:, None]
