@@ -1,0 +1,206 @@
+"""Benchmark of one ring member's attention share on one MI355X.
+
+A step is one ra_share_forward call: rank `rank`'s resident query block against all
+N K/V blocks of the sequence in ring order, online softmax, final rescale.  Inputs
+are seeded synthetic tensors already resident in GPU memory.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+KERNEL_SRC = os.path.join(ROOT, "long_context_exact_ra_amd", "csrc", "fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_share_L128K_N8.json")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_per_launch(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha() or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--step-path", action="store_true",
+                   help="also time the per-step path (N x ra_step + ra_finalize)")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the ring transport across GPUs is not built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from long_context_exact_ra_amd import ra, synth
+
+    if args.copy_calib:
+        copy_calibration()
+        return
+
+    name = args.workload or synth.HEADLINE
+    w = synth.WORKLOADS[name]
+    if w.dtype != "bf16" or w.full_q:
+        raise SystemExit("bench workloads are the bf16 single-share configurations")
+    dev = torch.device("cuda:0")
+    ra.load()
+    print(f"[bench] drawing {name}", file=sys.stderr, flush=True)
+    q, k, v = synth.draw_workload(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    scale = 1.0 / math.sqrt(w.d)
+    O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
+
+    def step():
+        ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, scale, O)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(f"[bench] {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    extra = {}
+    if args.step_path:
+        O_acc = torch.empty_like(O)
+        m = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
+        s = torch.empty_like(m)
+        sched = ra.ring_schedule(w.rank, w.N)
+
+        def step_path():
+            ra.state_init(O_acc, m, s)
+            for j in sched:
+                ra.step(qd, kd[:, :, j * w.l:(j + 1) * w.l], vd[:, :, j * w.l:(j + 1) * w.l],
+                        O_acc, m, s, scale)
+            ra.finalize(O_acc, s)
+
+        step_path()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(max(1, args.steps // 2)):
+            step_path()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        sp_ms = t0.elapsed_time(t1) / max(1, args.steps // 2)
+        extra["step_path"] = {"ms": round(sp_ms, 4),
+                              "tflops": round(flops / (sp_ms * 1e-3) / 1e12, 2)}
+
+    traffic = traffic_per_launch(name)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic}
+
+    cpu_baseline = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        Q, K, V = (synth.to_oracle_array(x) for x in (q, k, v))
+        threads = oracle.max_threads()
+        per_row = 4.0 * w.L * w.d
+        probe_rows = synth.sample_rows(w.B, w.H, w.l, 1, w.seed)[: max(8, threads)]
+        t = time.perf_counter()
+        oracle.share(Q, K, V, scale, w.rank, w.N, rows=probe_rows)
+        probe_s = time.perf_counter() - t
+        n_rows = int(max(len(probe_rows), len(probe_rows) * args.cpu_seconds / max(probe_s, 1e-3)))
+        n_rows = min(n_rows, w.B * w.H * w.l)
+        g = torch.Generator().manual_seed(w.seed + 11)
+        rows = sorted(set(torch.randint(0, w.B * w.H * w.l, (n_rows,), generator=g).tolist()))
+        print(f"[bench] oracle baseline on {len(rows)} rows, {threads} threads",
+              file=sys.stderr, flush=True)
+        t = time.perf_counter()
+        ref, _, _ = oracle.share(Q, K, V, scale, w.rank, w.N, rows=rows)
+        cpu_s = time.perf_counter() - t
+        cpu_tflops = len(rows) * per_row / cpu_s / 1e12
+        cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": threads,
+                        "kind": "oracle",
+                        "sample": f"{len(rows)} random query rows of the same share "
+                                  f"({len(rows) * per_row:.3e} FLOP, {cpu_s:.1f} s, fp64)"}
+        got = O.reshape(-1, w.d)[torch.tensor(rows, device=dev)].double().cpu().numpy()
+        err = np.abs(got - ref)
+        parity = {"rows": len(rows), "max_abs_err": float(err.max()),
+                  "ok": bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))}
+
+    line = {
+        "metric": "ring-share attention TFLOP/s (bf16) + % of MFMA peak at L=128K, N=8",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal Q/K/V, resident in HBM)",
+        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d, "L": w.L,
+                   "N": w.N, "rank": w.rank, "l": w.l, "flops_per_step": flops},
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "parity": parity,
+        "kernel_sha": kernel_sha(),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

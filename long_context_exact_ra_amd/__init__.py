@@ -1,0 +1,9 @@
+"""Ring-attention share on AMD MI355X (gfx950).
+
+`ra` is the binding of the C ABI in include/ra.h (libra.so, built by
+`python -m long_context_exact_ra_amd.build`); `synth` draws seeded inputs.
+The binding loads the library on first use and raises if it is missing.
+"""
+from . import ra, synth  # noqa: F401
+from .ra import (RaError, finalize, kv_head, ring_block, ring_schedule,  # noqa: F401
+                 share_forward, state_init, step)

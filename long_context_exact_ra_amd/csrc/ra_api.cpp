@@ -1,0 +1,229 @@
+// ra_api.cpp -- the C ABI of the ring-attention share library (include/ra.h):
+// argument validation, the ring schedule, the grouped-query head map, and
+// dispatch to the gfx950 kernels.  Validation happens before any HIP call, so a
+// rejected call neither touches the device nor enqueues work.
+#include "../../include/ra.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return RA_EHIP;
+}
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char *v = std::getenv("RA_DEBUG");
+        return v && v[0] && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+// After a launch: report a launch error, and in RA_DEBUG mode wait for the
+// stream so that a fault is attributed to the call that caused it.
+int after_launch(hipError_t e, hipStream_t st) {
+    if (e != hipSuccess) return hip_fail(e);
+    if (debug_sync()) {
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return RA_OK;
+}
+
+// 0 unknown, 1 gfx950, 2 other architecture; indexed by device ordinal.
+std::atomic<int> g_device_kind[64];
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev >= 0 && dev < 64) {
+        const int k = g_device_kind[dev].load(std::memory_order_relaxed);
+        if (k == 1) return RA_OK;
+        if (k == 2) return RA_ENOTSUP;
+    }
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    const bool ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) g_device_kind[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? RA_OK : RA_ENOTSUP;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool ptr_ok(const void *p) { return p != nullptr && aligned16(p); }
+
+bool opt_ptr_ok(const void *p) { return p == nullptr || aligned16(p); }
+
+bool heads_ok(int32_t B, int32_t H, int32_t H_kv, int32_t d, int32_t dtype) {
+    return B >= 1 && H >= 1 && H_kv >= 1 && H % H_kv == 0 && (d == 64 || d == 128) &&
+           (dtype == RA_F32 || dtype == RA_BF16);
+}
+
+bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
+// Work-group count of the forward kernels; false if it does not fit a 1-D grid.
+bool grid_size(int32_t B, int32_t H, int64_t l_q, int32_t dtype, int32_t *n_qtiles,
+               int32_t *n_wg) {
+    const int64_t tile = dtype == RA_BF16 ? ra::kBf16QueryTile : ra::kF32QueryTile;
+    const int64_t qt = (l_q + tile - 1) / tile;
+    const int64_t total = qt * (int64_t)B * H;
+    if (qt > INT32_MAX || total > INT32_MAX) return false;
+    *n_qtiles = (int32_t)qt;
+    *n_wg = (int32_t)total;
+    return true;
+}
+
+int launch_fwd(const ra::FwdArgs &a, int32_t B, int32_t d, int32_t dtype, int mode,
+               hipStream_t st) {
+    const hipError_t e = dtype == RA_BF16 ? ra::launch_fwd_bf16(a, B, d, mode, st)
+                                          : ra::launch_fwd_f32(a, B, d, mode, st);
+    return after_launch(e, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ra_ring_block(int32_t rank, int32_t N, int32_t t) {
+    if (N < 1 || rank < 0 || rank >= N || t < 0 || t >= N) return -RA_EINVAL;
+    // (rank - t) mod N with the non-negative remainder; both are in [0, N).
+    const int32_t j = rank - t;
+    return j < 0 ? j + N : j;
+}
+
+int ra_ring_schedule(int32_t rank, int32_t N, int32_t *out) {
+    if (N < 1 || rank < 0 || rank >= N || out == nullptr) return RA_EINVAL;
+    for (int32_t t = 0; t < N; ++t) out[t] = ra_ring_block(rank, N, t);
+    return RA_OK;
+}
+
+int32_t ra_kv_head(int32_t h, int32_t H, int32_t H_kv) {
+    if (H < 1 || H_kv < 1 || H % H_kv != 0 || h < 0 || h >= H) return -RA_EINVAL;
+    return h / (H / H_kv);
+}
+
+int ra_state_init(float *O_acc, float *m, float *l, const ra_shape *s, void *stream) {
+    if (s == nullptr || !heads_ok(s->B, s->H, s->H_kv, s->d, s->dtype) || s->l_q < 0)
+        return RA_EINVAL;
+    const int64_t rows = (int64_t)s->B * s->H * s->l_q;
+    if (rows == 0) return RA_OK;
+    if (!ptr_ok(O_acc) || !ptr_ok(m) || !ptr_ok(l)) return RA_EINVAL;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    return after_launch(ra::launch_state_init(O_acc, m, l, rows, s->d, st), st);
+}
+
+int ra_step(const void *Q_i, const void *K_blk, const void *V_blk, float *O_acc, float *m,
+            float *l, float scale, const ra_shape *s, void *stream) {
+    if (s == nullptr || !heads_ok(s->B, s->H, s->H_kv, s->d, s->dtype) || s->l_q < 0 ||
+        s->l_kv < 0 || !scale_ok(scale) || s->kv_head_stride < 0 || s->kv_batch_stride < 0)
+        return RA_EINVAL;
+    const int64_t blk = s->l_kv * s->d;
+    const int64_t hs = s->kv_head_stride ? s->kv_head_stride : blk;
+    const int64_t bs = s->kv_batch_stride ? s->kv_batch_stride : (int64_t)s->H_kv * hs;
+    if (hs < blk || hs % 8 != 0 || bs % 8 != 0 || bs < (int64_t)(s->H_kv - 1) * hs + blk)
+        return RA_EINVAL;
+    if (s->l_q == 0 || s->l_kv == 0) return RA_OK;
+    if (!ptr_ok(Q_i) || !ptr_ok(K_blk) || !ptr_ok(V_blk) || !ptr_ok(O_acc) || !ptr_ok(m) ||
+        !ptr_ok(l))
+        return RA_EINVAL;
+    ra::FwdArgs a{};
+    if (!grid_size(s->B, s->H, s->l_q, s->dtype, &a.n_qtiles, &a.n_wg)) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    a.Q = Q_i;
+    a.K = K_blk;
+    a.V = V_blk;
+    a.O = O_acc;
+    a.m = m;
+    a.l = l;
+    a.l_q = s->l_q;
+    a.blk_rows = s->l_kv;
+    a.kv_head_stride = hs;
+    a.kv_batch_stride = bs;
+    a.n_blocks = 1;
+    a.rank = 0;
+    a.H = s->H;
+    a.H_kv = s->H_kv;
+    a.group = s->H / s->H_kv;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return launch_fwd(a, s->B, s->d, s->dtype, ra::MODE_STEP, (hipStream_t)stream);
+}
+
+int ra_finalize(float *O_acc, const float *l, const ra_shape *s, void *O_out, void *stream) {
+    if (s == nullptr || !heads_ok(s->B, s->H, s->H_kv, s->d, s->dtype) || s->l_q < 0)
+        return RA_EINVAL;
+    const int64_t rows = (int64_t)s->B * s->H * s->l_q;
+    if (rows == 0) return RA_OK;
+    if (!ptr_ok(O_acc) || !ptr_ok(l) || !opt_ptr_ok(O_out)) return RA_EINVAL;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    return after_launch(ra::launch_finalize(O_acc, l, rows, s->d, s->dtype, O_out, st), st);
+}
+
+int ra_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                     int32_t d, int32_t B, int32_t dtype, const void *Q_i, const void *K,
+                     const void *V, float scale, float *O, float *m_out, float *l_out,
+                     void *O_cast, int32_t *sched_trace, void *stream) {
+    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
+        !heads_ok(B, H, H_kv, d, dtype) || !scale_ok(scale))
+        return RA_EINVAL;
+    if (L == 0) return RA_OK;
+    if (!ptr_ok(Q_i) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(O) || !opt_ptr_ok(m_out) ||
+        !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast) ||
+        (sched_trace != nullptr && ((uintptr_t)sched_trace & 3u) != 0))
+        return RA_EINVAL;
+    const int64_t l = L / N;
+    ra::FwdArgs a{};
+    if (!grid_size(B, H, l, dtype, &a.n_qtiles, &a.n_wg)) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    a.Q = Q_i;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.m = m_out;
+    a.l = l_out;
+    a.O_cast = O_cast;
+    a.trace = sched_trace;
+    a.l_q = l;
+    a.blk_rows = l;
+    a.kv_head_stride = L * d;
+    a.kv_batch_stride = (int64_t)H_kv * L * d;
+    a.n_blocks = N;
+    a.rank = rank;
+    a.H = H;
+    a.H_kv = H_kv;
+    a.group = H / H_kv;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return launch_fwd(a, B, d, dtype, ra::MODE_SHARE, (hipStream_t)stream);
+}
+
+const char *ra_strerror(int status) {
+    switch (status) {
+    case RA_OK: return "success";
+    case RA_EINVAL: return "invalid argument";
+    case RA_ENOTSUP: return "unsupported device or size (needs gfx950)";
+    case RA_EHIP: return "HIP runtime error (see ra_last_hip_error)";
+    default: return "unknown status";
+    }
+}
+
+int ra_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

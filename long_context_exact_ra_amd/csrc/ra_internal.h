@@ -1,0 +1,57 @@
+// ra_internal.h -- shared declarations between the C ABI layer and the kernel
+// translation units of the ring-attention share library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Work description for one launch of the forward kernels.
+//
+// The launch covers every (batch, query head, query tile) of the resident block.
+// Each work-group walks the K/V blocks in ring order: at step t it reads block
+// j(t) = (rank - t) mod n_blocks (slowleelab "Ring Attention" page, L3 and 4.2),
+// i.e. rows j*blk_rows .. (j+1)*blk_rows - 1 of the K/V head it is mapped to.
+// A single ring step (ra_step) is n_blocks = 1, rank = 0 over a block pointer.
+struct FwdArgs {
+    const void *Q;   // [B, H, l_q, D] contiguous
+    const void *K;   // head (b, g) starts at K + b*kv_batch_stride + g*kv_head_stride
+    const void *V;
+    float *O;        // share: finalised output; step: running O_acc (in/out)
+    float *m;        // share: row max out (nullable); step: running max (in/out)
+    float *l;        // share: row sum out (nullable); step: running sum (in/out)
+    void *O_cast;    // share only, nullable: output in the input dtype
+    int32_t *trace;  // share only, nullable: block index used at each step
+    int64_t l_q;
+    int64_t blk_rows;
+    int64_t kv_head_stride;
+    int64_t kv_batch_stride;
+    int32_t n_blocks;
+    int32_t rank;
+    int32_t H;
+    int32_t H_kv;
+    int32_t group;     // H / H_kv
+    int32_t n_qtiles;  // query tiles per (batch, head)
+    int32_t n_wg;      // total work-groups of the launch
+    float scale;       // score scale (normally 1/sqrt(d))
+    float scale_log2;  // scale * log2(e): exponentials are taken as exp2
+};
+
+enum Mode : int {
+    MODE_SHARE = 0,  // no state in; finalised output out
+    MODE_STEP = 1    // running state in and out, no division
+};
+
+// Query rows per work-group of each kernel (the host sizes the grid with these).
+constexpr int kBf16QueryTile = 256;
+constexpr int kF32QueryTile = 64;
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, int B, int d, int mode, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdArgs &a, int B, int d, int mode, hipStream_t st);
+hipError_t launch_state_init(float *O_acc, float *m, float *l, int64_t rows, int d,
+                             hipStream_t st);
+hipError_t launch_finalize(float *O_acc, const float *l, int64_t rows, int d, int dtype,
+                           void *O_out, hipStream_t st);
+
+}  // namespace ra

@@ -1,0 +1,156 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, its host-only functions are bit-exact, and every argument check rejects
+bad input before touching the device (fake device addresses are never read)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from long_context_exact_ra_amd import ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ra.lib_path()),
+                                reason="libra.so not built (python -m long_context_exact_ra_amd.build)")
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "ra.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ra.load()
+    declared = _declared_symbols()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(ra.exported_symbols()) == declared
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 64, 127, 128])
+def test_ring_schedule_bit_exact(N):
+    for rank in range(N):
+        assert ra.ring_schedule(rank, N) == oracle.ring_schedule(rank, N)
+        for t in range(N):
+            assert ra.ring_block(rank, N, t) == oracle.ring_schedule(rank, N)[t]
+
+
+def test_ring_block_rejects_bad_arguments():
+    for args in [(0, 0, 0), (-1, 4, 0), (4, 4, 0), (0, 4, -1), (0, 4, 4)]:
+        assert ra.ring_block(*args) == -ra.RA_EINVAL
+    lib = ra.load()
+    out = (ctypes.c_int32 * 4)()
+    assert lib.ra_ring_schedule(0, 0, out) == ra.RA_EINVAL
+    assert lib.ra_ring_schedule(4, 4, out) == ra.RA_EINVAL
+    assert lib.ra_ring_schedule(0, 4, None) == ra.RA_EINVAL
+
+
+def test_kv_head_map():
+    assert [ra.kv_head(h, 28, 4) for h in range(28)] == [oracle.kv_head(h, 28, 4) for h in range(28)]
+    assert ra.kv_head(0, 6, 4) == -ra.RA_EINVAL
+    assert ra.kv_head(6, 6, 3) == -ra.RA_EINVAL
+
+
+def test_strerror():
+    for code in (0, 1, 2, 3):
+        assert ra.load().ra_strerror(code)
+    assert ra.load().ra_last_hip_error() == 0
+
+
+# Fake but 16-byte aligned "device" addresses: validation must reject before use.
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)
+
+
+def _share(**kw):
+    args = dict(rank=3, N=8, L=8 * 64, H=4, H_kv=2, d=128, B=1, dtype=ra.RA_BF16, Q=P, K=P,
+                V=P, scale=0.088, O=P2, m=None, l=None, cast=None, trace=None, stream=None)
+    args.update(kw)
+    return ra.load().ra_share_forward(
+        args["rank"], args["N"], args["L"], args["H"], args["H_kv"], args["d"], args["B"],
+        args["dtype"], args["Q"], args["K"], args["V"], args["scale"], args["O"], args["m"],
+        args["l"], args["cast"], args["trace"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(N=0), dict(rank=-1), dict(rank=8), dict(L=8 * 64 + 1), dict(L=-8),
+    dict(H=5), dict(H_kv=0), dict(d=96), dict(d=256), dict(B=0), dict(dtype=7),
+    dict(scale=0.0), dict(scale=-1.0), dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(Q=None), dict(K=None), dict(V=None), dict(O=None), dict(Q=MIS), dict(O=MIS),
+    dict(m=MIS), dict(cast=MIS), dict(trace=ctypes.c_void_p(0x10002)),
+])
+def test_share_forward_rejects(kw):
+    assert _share(**kw) == ra.RA_EINVAL
+
+
+def test_share_forward_empty_sequence_is_noop():
+    assert _share(L=0, Q=None, K=None, V=None, O=None) == ra.RA_OK
+
+
+def _shape(**kw):
+    s = ra.RaShape(B=1, H=4, H_kv=2, d=128, l_q=100, l_kv=64, kv_head_stride=0,
+                   kv_batch_stride=0, dtype=ra.RA_BF16)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _step(s, scale=0.1, ptrs=None):
+    p = ptrs or [P] * 6
+    return ra.load().ra_step(*p, scale, ctypes.byref(s), None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=0), dict(H=3), dict(H_kv=0), dict(d=32), dict(dtype=2), dict(l_q=-1),
+    dict(l_kv=-1), dict(kv_head_stride=64 * 128 - 8), dict(kv_head_stride=64 * 128 + 4),
+    dict(kv_batch_stride=12), dict(kv_head_stride=-8),
+])
+def test_step_rejects_bad_shape(kw):
+    assert _step(_shape(**kw)) == ra.RA_EINVAL
+
+
+def test_step_rejects_bad_pointers_and_scale():
+    s = _shape()
+    assert _step(s, scale=0.0) == ra.RA_EINVAL
+    assert _step(s, scale=float("nan")) == ra.RA_EINVAL
+    for i in range(6):
+        ptrs = [P] * 6
+        ptrs[i] = None
+        assert _step(s, ptrs=ptrs) == ra.RA_EINVAL
+        ptrs[i] = MIS
+        assert _step(s, ptrs=ptrs) == ra.RA_EINVAL
+    assert ra.load().ra_step(P, P, P, P, P, P, 0.1, None, None) == ra.RA_EINVAL
+
+
+def test_step_empty_is_noop():
+    assert _step(_shape(l_q=0), ptrs=[None] * 6) == ra.RA_OK
+    assert _step(_shape(l_kv=0), ptrs=[None] * 6) == ra.RA_OK
+
+
+def test_finalize_and_init_validation():
+    lib = ra.load()
+    s = _shape()
+    assert lib.ra_finalize(None, P, ctypes.byref(s), None, None) == ra.RA_EINVAL
+    assert lib.ra_finalize(P, MIS, ctypes.byref(s), None, None) == ra.RA_EINVAL
+    assert lib.ra_finalize(P, P, ctypes.byref(s), MIS, None) == ra.RA_EINVAL
+    assert lib.ra_finalize(P, P, None, None, None) == ra.RA_EINVAL
+    assert lib.ra_state_init(P, None, P, ctypes.byref(s), None) == ra.RA_EINVAL
+    assert lib.ra_state_init(P, P, P, None, None) == ra.RA_EINVAL
+    empty = _shape(l_q=0)
+    assert lib.ra_finalize(None, None, ctypes.byref(empty), None, None) == ra.RA_OK
+    assert lib.ra_state_init(None, None, None, ctypes.byref(empty), None) == ra.RA_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros((1, 2, 4, 64))
+    k = torch.zeros((1, 2, 16, 64))
+    o = torch.zeros((1, 2, 4, 64))
+    with pytest.raises(ValueError):
+        ra.share_forward(0, 4, 16, 2, 2, 64, 1, q, k, k, 0.125, o)
