@@ -22,15 +22,19 @@
 //    O^T = V^T P^T: no cross-lane shuffle of P.  The key order inside each
 //    16-deep contraction is permuted to match the score layout, and V^T is read
 //    from LDS with ds_read_b64_tr_b16 transpose loads using the same permutation.
-//  * K/V tiles (64 keys) are double-buffered in LDS: the next tile's global loads
-//    are issued before the current tile's math and written to the other buffer
-//    after it; one barrier per tile.  Row pitches are padded against bank
-//    conflicts (K: +16 B for the 16-byte row reads, V: +32 B for the 4-row
-//    transpose reads).
+//  * Software pipeline inside each wave: iteration j computes the scores of tile
+//    j+1, then issues the P V products of tile j interleaved with the softmax
+//    (exp2, bf16 packing, row sums) of tile j+1, so matrix-core and vector-ALU work
+//    of one wave co-issue; the second wave on the SIMD fills the remaining gaps.
+//  * K and V tiles (64 keys) are double-buffered in LDS separately (K one tile
+//    ahead of V); the next tiles' global loads are issued at the top of an
+//    iteration and written to LDS at its end; one barrier per iteration.  Row
+//    pitches are padded against bank conflicts (K: +16 B for 16-byte row reads,
+//    V: +32 B for the 4-row transpose reads).
 //  * The exponent reference is updated lazily: the O / l rescale only runs when
 //    some row's maximum grew by more than 2^kTau (a wave-uniform branch), so
 //    exp2(s*c - R) stays <= 2^kTau.  The true running maximum is tracked
-//    separately, and the state is converted to it at the end, so outputs obey
+//    separately and the state is converted to it at the end, so outputs obey
 //    m = exact running maximum.
 //  * Work-group ids are remapped so each XCD (8 per chip, one L2 each) works on a
 //    contiguous range of (batch, head, query tile): the work-groups sharing a K/V
@@ -43,6 +47,7 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -56,6 +61,12 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
     const int per = n / 8, rem = n % 8;
     const int xcd = wg % 8, slot = wg / 8;
     return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Ring order: at step t, member `rank` works on block (rank - t) mod n.
+__device__ __forceinline__ int64_t ring_block(int32_t rank, int64_t t, int32_t n) {
+    int64_t j = (int64_t)rank - t;
+    return j < 0 ? j + n : j;
 }
 
 // Value of x in lane (lane ^ 32), via the gfx950 half-swap.
@@ -72,39 +83,67 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16 *p) {
         (bf16x4 __attribute__((address_space(3))) *)(p));
 }
 
+// Position of one K/V tile in the ring walk, advanced without divisions.
+struct TileCursor {
+    int32_t t;    // ring step
+    int32_t tin;  // tile index inside the block
+    __device__ __forceinline__ void next(int32_t tiles_per_blk) {
+        if (++tin == tiles_per_blk) {
+            tin = 0;
+            ++t;
+        }
+    }
+};
+
 template <int D>
 struct Tile {
-    static constexpr int KP = D + 8;       // K row pitch (elements)
-    static constexpr int VP = D + 16;      // V row pitch (elements)
-    static constexpr int CPR = D / 8;      // 16-byte chunks per row
-    static constexpr int PT = BC * CPR / NT;  // chunks per thread per tensor
-    static_assert(PT >= 1 && BC * CPR % NT == 0, "tile split");
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int RPL = 64 / CPR;         // rows filled by one wave-wide load
+    static constexpr int ROUND = RPL * (NT / 64);  // rows filled by one load of every wave
+    static constexpr int LOADS = BC / ROUND;     // loads per wave per tensor
+    static_assert(LOADS >= 1 && BC % ROUND == 0, "tile split");
 };
+
+// LDS tile layouts: rows of D bf16 without padding; the 16-byte chunk c of row r
+// sits at position c ^ swz(r).  K rows are read 16 bytes per lane by 32 rows at
+// once (swz = r & 7 spreads 8 rows over 8 distinct chunk slots); V rows are read by
+// 4-row x 32-byte transpose loads (swz = 2*(r & 3) keeps chunk pairs together and
+// spreads 4 rows over 4 distinct 32-byte slots).
+__device__ __forceinline__ int swz_k(int r) { return r & 7; }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
 
 template <int D, int MODE>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     using T = Tile<D>;
-    constexpr int KP = T::KP, VP = T::VP, PT = T::PT, CPR = T::CPR;
+    constexpr int CPR = T::CPR, RPL = T::RPL, ROUND = T::ROUND, LOADS = T::LOADS;
     constexpr int NKK = D / 16;  // 16-deep contractions over the head dimension
     constexpr int NDT = D / 32;  // 32-wide output tiles over the head dimension
+    constexpr int TILE = BC * D;  // elements per K or V tile
 
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][BC * KP];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[2][BC * VP];
+    __shared__ __attribute__((aligned(1024))) bf16 K0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 K1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 V0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 V1[TILE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
     const int hf = lane >> 5, ln = lane & 31;
     const int g16 = lane >> 4, i16 = lane & 15;
 
-    const int wg = xcd_remap(blockIdx.x, a.n_wg);
-    const int qt = wg % a.n_qtiles;
-    const int bh = wg / a.n_qtiles;
-    const int h = bh % a.H, b = bh / a.H;
-    const int g = h / a.group;
+    // Work-group coordinates are uniform; integer division would otherwise leave them
+    // in VGPRs.
+    const int wg = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, a.n_wg));
+    const int qt = __builtin_amdgcn_readfirstlane(wg % a.n_qtiles);
+    const int bh = __builtin_amdgcn_readfirstlane(wg / a.n_qtiles);
+    const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
+    const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
+    const int g = __builtin_amdgcn_readfirstlane(h / a.group);
 
-    const int64_t q = (int64_t)qt * BR + wave * 32 + ln;
-    const bool qvalid = q < a.l_q;
-    const int64_t qrow = (int64_t)bh * a.l_q + q;  // flat row of Q / O / m / l
+    // Flat row of Q / O / m / l = row_base (uniform) + qloc (this lane's row).
+    const int64_t row_base = (int64_t)bh * a.l_q + (int64_t)qt * BR;
+    const int qloc = wave * 32 + ln;
+    const bool qvalid = (int64_t)qt * BR + qloc < a.l_q;
 
     const bf16 *Kh = (const bf16 *)a.K + b * a.kv_batch_stride + g * a.kv_head_stride;
     const bf16 *Vh = (const bf16 *)a.V + b * a.kv_batch_stride + g * a.kv_head_stride;
@@ -112,7 +151,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     // Resident Q fragment: B operand of S^T = K Q^T, lane holds Q[q][16kk+8hf .. +7].
     bf16x8 qf[NKK];
     {
-        const bf16 *qp = (const bf16 *)a.Q + qrow * D + 8 * hf;
+        const bf16 *qp = (const bf16 *)a.Q + row_base * D + (qloc * D + 8 * hf);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             if (qvalid) qf[kk] = *(const bf16x8 *)(qp + 16 * kk);
@@ -122,163 +161,267 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
 
     // Running state per lane (query row ln; lane halves hold different d / keys).
     f32x16 o[NDT];
-    float lsum = 0.f;            // this half's partial row sum, relative to R
-    float R = -INFINITY;         // exponent reference, log2 units
-    float m_nat = -INFINITY;     // exact running max of scale * S
+    float lsum = 0.f;         // this half's partial row sum, relative to R
+    float R = -INFINITY;      // exponent reference, log2 units
+    float m_nat = -INFINITY;  // exact running max of scale * S
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        o[dt] = f32x16{};
+        asm volatile("" : "+v"(o[dt]));  // no special-cased first products
+    }
     if constexpr (MODE == MODE_STEP) {
         if (qvalid) {
-            m_nat = a.m[qrow];
+            m_nat = a.m[row_base + qloc];
             R = m_nat * kLog2e;
-            if (hf == 0) lsum = a.l[qrow];
-            const float *op = a.O + qrow * D + 4 * hf;
+            if (hf == 0) lsum = a.l[row_base + qloc];
+            const float *op = a.O + row_base * D + (qloc * D + 4 * hf);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const f32x4 v = *(const f32x4 *)(op + 32 * dt + 8 * i4);
-                    o[dt][4 * i4 + 0] = v[0];
-                    o[dt][4 * i4 + 1] = v[1];
-                    o[dt][4 * i4 + 2] = v[2];
-                    o[dt][4 * i4 + 3] = v[3];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[dt][4 * i4 + e] = v[e];
                 }
-        } else {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
         }
-    } else {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     }
 
     const float c = a.scale_log2;
-    const int64_t tiles_per_blk = (a.blk_rows + BC - 1) / BC;
-    const int64_t n_tiles = tiles_per_blk * a.n_blocks;
+    // The host guarantees the tile count of a launch fits in int32.
+    const int32_t tiles_per_blk = (int32_t)((a.blk_rows + BC - 1) / BC);
+    const int32_t n_tiles = tiles_per_blk * a.n_blocks;
 
-    // Global -> register staging of one K/V tile.
-    uint4 kreg[PT], vreg[PT];
-    auto load_tile = [&](int64_t it) {
-        const int64_t t = it / tiles_per_blk;
-        const int64_t tin = it - t * tiles_per_blk;
-        int64_t j = (int64_t)a.rank - t;
-        if (j < 0) j += a.n_blocks;
-        const int64_t row0 = j * a.blk_rows + tin * BC;
-        const int64_t nvalid = a.blk_rows - tin * BC;
+    // ---- direct global -> LDS tile loads (no staging registers).  Load p of wave w
+    // fills tile rows p*ROUND + w*RPL + lane/CPR; lane % CPR is the chunk slot.  Both
+    // swizzles depend only on row % 8 = (w*RPL + lane/CPR) % 8, so one per-lane byte
+    // offset per tensor serves every load; only the wave-uniform bases move.
+    const int lrow = wave * RPL + lane / CPR;  // row of load 0
+    const uint32_t koff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_k(lrow)) * 8) * 2;
+    const uint32_t voff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_v(lrow)) * 8) * 2;
+    auto load_tile = [&](const bf16 *base, const TileCursor &cur, bf16 *dst, uint32_t off,
+                         bool is_v) {
+        const int64_t row0 =
+            ring_block(a.rank, cur.t, a.n_blocks) * a.blk_rows + (int64_t)cur.tin * BC;
+        const int64_t left = a.blk_rows - (int64_t)cur.tin * BC;  // keys left in the block
+        const char *tile = (const char *)(base + row0 * D);  // wave-uniform
+        // Opaque per call, so the compiler keeps the offset 32-bit (SGPR base + VGPR
+        // offset addressing) instead of hoisting a 64-bit copy of it.
+        asm volatile("" : "+v"(off));
+        bf16 *ldst = dst + wave * RPL * D;
+        if (left >= BC) {
 #pragma unroll
-        for (int p = 0; p < PT; ++p) {
-            const int cidx = tid + NT * p;
-            const int r = cidx / CPR, cc = cidx % CPR;
-            if (r < nvalid) {
-                const int64_t off = (row0 + r) * D + cc * 8;
-                kreg[p] = *(const uint4 *)(Kh + off);
-                vreg[p] = *(const uint4 *)(Vh + off);
-            } else {
-                kreg[p] = make_uint4(0, 0, 0, 0);
-                vreg[p] = make_uint4(0, 0, 0, 0);
+            for (int p = 0; p < LOADS; ++p)
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(tile + (size_t)p * ROUND * D * 2 + off),
+                    (void __attribute__((address_space(3))) *)(ldst + p * ROUND * D), 16, 0, 0);
+        } else {
+            // Ragged tail: rows past the block end repeat its last row; those keys are
+            // masked, so their probabilities are exactly 0.
+            const int last = (int)left - 1;
+            int ln2 = lane;
+            asm volatile("" : "+v"(ln2));  // recompute the slot here (rare path)
+            const int lr = wave * RPL + ln2 / CPR;
+            const int slot = (ln2 % CPR) ^ (is_v ? swz_v(lr) : swz_k(lr));
+#pragma unroll
+            for (int p = 0; p < LOADS; ++p) {
+                const int r = p * ROUND + lr;
+                const int rr = r < last ? r : last;
+                const uint32_t o2 = (uint32_t)(rr * D + slot * 8) * 2;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(tile + o2),
+                    (void __attribute__((address_space(3))) *)(ldst + p * ROUND * D), 16, 0, 0);
             }
         }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < PT; ++p) {
-            const int cidx = tid + NT * p;
-            const int r = cidx / CPR, cc = cidx % CPR;
-            *(uint4 *)(&Ks[buf][r * KP + cc * 8]) = kreg[p];
-            *(uint4 *)(&Vs[buf][r * VP + cc * 8]) = vreg[p];
-        }
-    };
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int64_t it = 0; it < n_tiles; ++it) {
-        const int buf = (int)(it & 1);
-        const int64_t t = it / tiles_per_blk;
-        const int64_t tin = it - t * tiles_per_blk;
-        if constexpr (MODE == MODE_SHARE) {
-            if (a.trace && tin == 0 && wg == 0 && tid == 0) {
-                int64_t j = (int64_t)a.rank - t;
-                if (j < 0) j += a.n_blocks;
-                a.trace[t] = (int32_t)j;
-            }
-        }
-        if (it + 1 < n_tiles) load_tile(it + 1);
-
-        // ---- S^T = K Q^T: two 32-key blocks, lane = query, 16 keys per lane each.
-        const bf16 *kt = Ks[buf];
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // ---- S^T = K Q^T for one tile: lane = query, 16 keys per lane per 32-key half.
+    // s0[i] / s1[i] hold key 8*(i/4) + 4*hf + i%4 (+32 for s1) of the tile.
+    f32x16 s0, s1;
+    // K fragment addresses: row ln (and ln + 32), chunk (2*kk + hf) ^ swz_k(ln).  With
+    // kk = 4*m + n the element offset is 64*m + (kbase ^ 16*n): the swizzle bits that
+    // touch kk (chunk bits 1-2) and the row / half bits are disjoint, so one per-lane
+    // base serves every read.
+    const int kbase = [&] {
+        const int sw = swz_k(ln);
+        return ln * D + 8 * (hf ^ (sw & 1)) + 16 * ((sw >> 1) & 3);
+    }();
+    auto scores = [&](const bf16 *kt, int64_t nvalid) {
+        s0 = f32x16{};
+        s1 = f32x16{};
+        int kb = kbase;
+        asm volatile("" : "+v"(kb));  // derive the read offsets here, not kept live
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            const bf16x8 k0 = *(const bf16x8 *)(kt + ln * KP + 16 * kk + 8 * hf);
-            const bf16x8 k1 = *(const bf16x8 *)(kt + (32 + ln) * KP + 16 * kk + 8 * hf);
+            const bf16 *kp = kt + (kb ^ (16 * (kk & 3))) + 64 * (kk >> 2);
+            const bf16x8 k0 = *(const bf16x8 *)(kp);
+            const bf16x8 k1 = *(const bf16x8 *)(kp + 32 * D);
             s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
+            if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
         }
-        // s0[i] / s1[i]: key 8*(i/4) + 4*hf + i%4 (+32 for s1) of this tile.
-        const int64_t nvalid = a.blk_rows - tin * BC;
         if (nvalid < BC) {
+            // key index = 8*(i/4) + i%4 + 4*hf: compare the constant part with a
+            // per-lane limit (no per-key registers).
+            const int lim = (int)nvalid - 4 * hf;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
-                if (key >= nvalid) s0[i] = -INFINITY;
-                if (key + 32 >= nvalid) s1[i] = -INFINITY;
+                const int kc = 8 * (i >> 2) + (i & 3);
+                if (kc >= lim) s0[i] = -INFINITY;
+                if (kc + 32 >= lim) s1[i] = -INFINITY;
             }
         }
+    };
 
-        // ---- row maximum (in-lane over 32 keys, then across the lane halves)
-        float mx = fmaxf(s0[0], s1[0]);
+    // Row max of the current scores (raw dot units), both lane halves combined.
+    auto row_max = [&]() {
+        float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s0[1], s1[1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-        mx = fmaxf(mx, other_half(mx));
-        m_nat = fmaxf(m_nat, mx * a.scale);
-        const float my = mx * c;
-        if (__builtin_amdgcn_ballot_w64(my > R + kTau)) {
-            const float Rn = fmaxf(R, my);
-            const float alpha = __builtin_amdgcn_exp2f(R - Rn);  // R = -inf gives 0
-            R = Rn;
-            lsum *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        for (int i = 2; i < 16; i += 2) {
+            ma = fmaxf(fmaxf(ma, s0[i]), s1[i]);
+            mb = fmaxf(fmaxf(mb, s0[i + 1]), s1[i + 1]);
         }
+        const float mx = fmaxf(ma, mb);
+        return fmaxf(mx, other_half(mx));
+    };
 
-        // ---- P^T = exp2(S^T c - R), row sums, bf16 packing into PV operands
+    // Softmax numerators of the current scores, packed into the four PV operands.
+    // Operand c4 covers keys 16*c4 + 8*(j/4) + 4*hf + j%4, j = 0..7.
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    auto softmax_part = [&](bf16x8 *pb, int part) {
         const float nR = -R;
-        bf16x8 pb[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, nR));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, nR));
-            lsum += p0 + p1;
-            pb[i >> 3][i & 7] = (bf16)p0;
-            pb[2 + (i >> 3)][i & 7] = (bf16)p1;
+        for (int e = 0; e < 8; e += 2) {
+            const int i = 8 * (part & 1) + e;
+            const f32x16 &s = (part < 2) ? s0 : s1;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, nR));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, nR));
+            const bf16x2 pk = {(bf16)p0, (bf16)p1};
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(ones, pk, lsum, false);
+            pb[part][e] = pk[0];
+            pb[part][e + 1] = pk[1];
         }
+    };
 
-        // ---- O^T += V^T P^T; contraction c4 covers keys 16*c4 + 8*(j/4) + 4*hf + j%4
-        const bf16 *vt = Vs[buf];
+    // O^T += V^T P^T for contraction c4 of a tile.  The 16 lanes of group g16 read
+    // rows 16*c4 + 4*hf + 0..3 (then +8) and head-dim columns 32*dt + 16*(g16&1) + 0..15,
+    // i.e. chunk 4*dt + x with x = 2*(g16&1) + (i16&3)/2, stored at (4*dt + x) ^ swz_v.
+    // With dt = 2*m + n that is 8*m + 4*(n ^ (sw >> 2)) + (x ^ (sw & 2)): two per-lane
+    // offsets (n = 0, 1) plus immediate offsets.
+    // voff(n) = vbase ^ (32*n): chunk bit 2 (n) is the only bit the two differ in.
+    const int vbase = [&] {
+        const int vrow = 4 * hf + (i16 >> 2);  // row within each 16-row contraction
+        const int sw = swz_v(vrow);            // rows 16*c4 + vrow (+8) share it
+        const int x = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+        return vrow * D + (4 * (sw >> 2) + (x ^ (sw & 2))) * 8 + 4 * (i16 & 1);
+    }();
+    auto pv_part = [&](const bf16 *vt, const bf16x8 *pb, int c4) {
+        int vb = vbase;
+        asm volatile("" : "+v"(vb));
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
+        for (int dt = 0; dt < NDT; ++dt) {
+            const bf16 *vp = vt + (vb ^ (32 * (dt & 1))) + 64 * (dt >> 1) + 16 * c4 * D;
+            const bf16x4 lo = tr_read(vp);
+            const bf16x4 hi = tr_read(vp + 8 * D);
+            const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c4], o[dt], 0, 0, 0);
+        }
+    };
+
+    // Raise the exponent reference to cover a new row maximum (raw units), lazily.
+    auto needs_rescale = [&](float mx) {
+        m_nat = fmaxf(m_nat, mx * a.scale);
+        return __builtin_amdgcn_ballot_w64(mx * c > R + kTau) != 0;
+    };
+    auto rescale = [&](float mx) {
+        const float Rn = fmaxf(R, mx * c);
+        const float alpha = __builtin_amdgcn_exp2f(R - Rn);  // R = -inf gives 0
+        R = Rn;
+        lsum *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const bf16 *vp = vt + (16 * c4 + 4 * hf + (i16 >> 2)) * VP + 32 * dt +
-                                 16 * (g16 & 1) + 4 * (i16 & 3);
-                const bf16x4 lo = tr_read(vp);
-                const bf16x4 hi = tr_read(vp + 8 * VP);
-                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c4], o[dt], 0, 0, 0);
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    };
+
+    // ---- prologue: K(0), K(1), V(0) into LDS; scores and softmax of tile 0.
+    TileCursor cK{0, 0}, cV{0, 0}, cS{0, 0};  // next K load, next V load, next scores
+    load_tile(Kh, cK, K0, koff_g, false);
+    cK.next(tiles_per_blk);
+    load_tile(Vh, cV, V0, voff_g, true);
+    cV.next(tiles_per_blk);
+    if (n_tiles > 1) {
+        load_tile(Kh, cK, K1, koff_g, false);
+        cK.next(tiles_per_blk);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
+    __syncthreads();
+
+    bf16x8 pp[4];  // packed softmax numerators of the tile whose P V product is next
+    {
+        scores(K0, a.blk_rows - (int64_t)cS.tin * BC);
+        cS.next(tiles_per_blk);
+        const float mx = row_max();
+        if (needs_rescale(mx)) rescale(mx);
+#pragma unroll
+        for (int part = 0; part < 4; ++part) softmax_part(pp, part);
+    }
+    // Iteration 0 overwrites K buffer 0, which every wave has just read.
+    __syncthreads();
+
+    // ---- main loop: iteration j = scores(j+1) + [PV(j) || softmax(j+1)].
+    // K(j+2) goes to the K buffer of tile j, V(j+1) to the V buffer of tile j-1.
+    auto iteration = [&](int32_t j, const bf16 *kcur, bf16 *knext, const bf16 *vcur,
+                         bf16 *vnext) {
+        if (j + 2 < n_tiles) {
+            load_tile(Kh, cK, knext, koff_g, false);
+            cK.next(tiles_per_blk);
+        }
+        if (j + 1 < n_tiles) {
+            load_tile(Vh, cV, vnext, voff_g, true);
+            cV.next(tiles_per_blk);
+            scores(kcur, a.blk_rows - (int64_t)cS.tin * BC);
+            cS.next(tiles_per_blk);
+            const float mx = row_max();
+            // P(j+1) overwrites P(j) operand by operand, after the product using it.
+            if (needs_rescale(mx)) {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    pv_part(vcur, pp, c4);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                rescale(mx);
+#pragma unroll
+                for (int part = 0; part < 4; ++part) softmax_part(pp, part);
+            } else {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    pv_part(vcur, pp, c4);
+                    softmax_part(pp, c4);
+                    __builtin_amdgcn_sched_barrier(0);  // keep operand lifetimes per stage
+                }
             }
+        } else {
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) pv_part(vcur, pp, c4);
         }
-
-        if (it + 1 < n_tiles) store_tile(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+    };
+    for (int32_t j = 0; j < n_tiles; j += 2) {
+        iteration(j, K1, K0, V0, V1);
+        if (j + 1 < n_tiles) iteration(j + 1, K0, K1, V1, V0);
     }
 
-    if (!qvalid || n_tiles == 0) return;
+    if constexpr (MODE == MODE_SHARE) {
+        // The ring order the loads above followed, one entry per step.
+        if (a.trace && wg == 0)
+            for (int t = tid; t < a.n_blocks; t += NT)
+                a.trace[t] = (int32_t)ring_block(a.rank, t, a.n_blocks);
+    }
+    if (!qvalid) return;
     const float ltot = lsum + other_half(lsum);
+    const int ooff = qloc * D + 4 * hf;  // this lane's output offset past row_base * D
     // o[dt][4*i4 + e]: head-dim index 32*dt + 8*i4 + 4*hf + e
     if constexpr (MODE == MODE_SHARE) {
-        float *op = a.O + qrow * D + 4 * hf;
+        float *op = a.O + row_base * D + ooff;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -288,17 +431,17 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
                 *(f32x4 *)(op + 32 * dt + 8 * i4) = v;
                 if (a.O_cast) {
                     bf16x4 cv = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-                    *(bf16x4 *)((bf16 *)a.O_cast + qrow * D + 4 * hf + 32 * dt + 8 * i4) = cv;
+                    *(bf16x4 *)((bf16 *)a.O_cast + row_base * D + ooff + 32 * dt + 8 * i4) = cv;
                 }
             }
         if (hf == 0) {
-            if (a.m) a.m[qrow] = m_nat;
-            if (a.l) a.l[qrow] = ltot * __builtin_amdgcn_exp2f(R - m_nat * kLog2e);
+            if (a.m) a.m[row_base + qloc] = m_nat;
+            if (a.l) a.l[row_base + qloc] = ltot * __builtin_amdgcn_exp2f(R - m_nat * kLog2e);
         }
     } else {
         // Re-express the state relative to the exact running maximum.
         const float f = __builtin_amdgcn_exp2f(R - m_nat * kLog2e);
-        float *op = a.O + qrow * D + 4 * hf;
+        float *op = a.O + row_base * D + ooff;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -308,8 +451,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
                 *(f32x4 *)(op + 32 * dt + 8 * i4) = v;
             }
         if (hf == 0) {
-            a.m[qrow] = m_nat;
-            a.l[qrow] = ltot * f;
+            a.m[row_base + qloc] = m_nat;
+            a.l[row_base + qloc] = ltot * f;
         }
     }
 }

@@ -4,7 +4,9 @@ Tolerances (written here, derived in the design notes):
   fp32 inputs: max |O_gpu - O_ref| <= 1e-5.
   bf16 inputs: |O_gpu - O_ref| <= 2e-2 + 1e-2 * |O_ref| elementwise.
   Statistics: m to 1e-5 (fp32) / 1e-3 + 1e-5|m| (bf16); lse = m + ln l to 1e-5 (1 + |lse|)
-  (fp32) / 2e-3 (bf16).  The ring schedule trace must match bit-exactly.
+  (fp32) / ln(1 + 2^-8) ~ 3.9e-3 (bf16: the row sum adds the bf16-rounded probabilities
+  that also weight V, each within 2^-9 relative, with a 2x margin for fp32 score and
+  exp2 error).  The ring schedule trace must match bit-exactly.
 """
 import math
 import sys
@@ -17,6 +19,8 @@ import oracle
 from long_context_exact_ra_amd import ra, synth
 
 pytestmark = pytest.mark.gpu
+
+LSE_TOL_BF16 = math.log1p(2.0 ** -8)
 
 
 def _say(msg):
@@ -56,7 +60,7 @@ def check_stats(m_gpu, l_gpu, M, Z, dtype, what=""):
     else:
         assert np.all(np.abs(m_gpu - M) <= 1e-3 + 1e-5 * np.abs(M)), \
             f"{what}: m err {np.abs(m_gpu - M).max():.3e}"
-        assert np.all(np.abs(lse_gpu - lse) <= 2e-3), \
+        assert np.all(np.abs(lse_gpu - lse) <= LSE_TOL_BF16), \
             f"{what}: lse err {np.abs(lse_gpu - lse).max():.3e}"
 
 
