@@ -105,12 +105,18 @@ struct Tile {
 };
 
 // LDS tile layouts: rows of D bf16 without padding; the 16-byte chunk c of row r
-// sits at position c ^ swz(r).  K rows are read 16 bytes per lane by 32 rows at
-// once (swz = r & 7 spreads 8 rows over 8 distinct chunk slots); V rows are read by
-// 4-row x 32-byte transpose loads (swz = 2*(r & 3) keeps chunk pairs together and
-// spreads 4 rows over 4 distinct 32-byte slots).
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+// sits at position c ^ swz(r).  The LDS serves 256 bytes per clock, so the
+// swizzles spread each read's lanes over distinct bytes of a 256-byte window:
+//  * K rows are read 16 bytes per lane by consecutive rows at one chunk: with 256-B
+//    rows (d = 128) swz_k = r & 15 puts 16 rows on 16 distinct 16-byte slots; with
+//    128-B rows (d = 64) rows alternate window halves and swz_k = (r >> 1) & 7.
+//  * V rows are read by 4-row transpose loads of 64 bytes (a chunk quad) per row: swz_v
+//    moves whole quads (XOR of chunk bits 2-3) so the 4 rows hit 4 distinct 64-byte
+//    windows: quad ^ (r & 3) for d = 128, quad ^ ((r >> 1) & 1) for d = 64.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 template <int D, int MODE>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
@@ -192,12 +198,13 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     const int32_t n_tiles = tiles_per_blk * a.n_blocks;
 
     // ---- direct global -> LDS tile loads (no staging registers).  Load p of wave w
-    // fills tile rows p*ROUND + w*RPL + lane/CPR; lane % CPR is the chunk slot.  Both
-    // swizzles depend only on row % 8 = (w*RPL + lane/CPR) % 8, so one per-lane byte
-    // offset per tensor serves every load; only the wave-uniform bases move.
+    // fills tile rows p*ROUND + w*RPL + lane/CPR; lane % CPR is the chunk slot.  One
+    // per-lane byte
+    // offset per tensor serves every load (loads are ROUND >= 32 rows apart and the
+    // swizzles repeat every 16 rows); only the wave-uniform bases move.
     const int lrow = wave * RPL + lane / CPR;  // row of load 0
-    const uint32_t koff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_k(lrow)) * 8) * 2;
-    const uint32_t voff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_v(lrow)) * 8) * 2;
+    const uint32_t koff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_k<D>(lrow)) * 8) * 2;
+    const uint32_t voff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_v<D>(lrow)) * 8) * 2;
     auto load_tile = [&](const bf16 *base, const TileCursor &cur, bf16 *dst, uint32_t off,
                          bool is_v) {
         const int64_t row0 =
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             int ln2 = lane;
             asm volatile("" : "+v"(ln2));  // recompute the slot here (rare path)
             const int lr = wave * RPL + ln2 / CPR;
-            const int slot = (ln2 % CPR) ^ (is_v ? swz_v(lr) : swz_k(lr));
+            const int slot = (ln2 % CPR) ^ (is_v ? swz_v<D>(lr) : swz_k<D>(lr));
 #pragma unroll
             for (int p = 0; p < LOADS; ++p) {
                 const int r = p * ROUND + lr;
@@ -237,13 +244,13 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     // ---- S^T = K Q^T for one tile: lane = query, 16 keys per lane per 32-key half.
     // s0[i] / s1[i] hold key 8*(i/4) + 4*hf + i%4 (+32 for s1) of the tile.
     f32x16 s0, s1;
-    // K fragment addresses: row ln (and ln + 32), chunk (2*kk + hf) ^ swz_k(ln).  With
-    // kk = 4*m + n the element offset is 64*m + (kbase ^ 16*n): the swizzle bits that
-    // touch kk (chunk bits 1-2) and the row / half bits are disjoint, so one per-lane
-    // base serves every read.
+    // K fragment addresses: row ln (and ln + 32, same swizzle), chunk (2*kk + hf) ^ sw.
+    // Element offset 8*((2*kk + hf) ^ sw) = 16*(kk ^ (sw >> 1)) + 8*(hf ^ (sw & 1)), so
+    // with kbase holding the sw terms the read for kk is at kbase ^ (16*kk): the kk bits
+    // (4..6) are disjoint from the row and half bits.
     const int kbase = [&] {
-        const int sw = swz_k(ln);
-        return ln * D + 8 * (hf ^ (sw & 1)) + 16 * ((sw >> 1) & 3);
+        const int sw = swz_k<D>(ln);
+        return ln * D + 8 * (hf ^ (sw & 1)) + 16 * (sw >> 1);
     }();
     auto scores = [&](const bf16 *kt, int64_t nvalid) {
         s0 = f32x16{};
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         asm volatile("" : "+v"(kb));  // derive the read offsets here, not kept live
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            const bf16 *kp = kt + (kb ^ (16 * (kk & 3))) + 64 * (kk >> 2);
+            const bf16 *kp = kt + (kb ^ (16 * kk));
             const bf16x8 k0 = *(const bf16x8 *)(kp);
             const bf16x8 k1 = *(const bf16x8 *)(kp + 32 * D);
             s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
@@ -304,22 +311,20 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
 
     // O^T += V^T P^T for contraction c4 of a tile.  The 16 lanes of group g16 read
     // rows 16*c4 + 4*hf + 0..3 (then +8) and head-dim columns 32*dt + 16*(g16&1) + 0..15,
-    // i.e. chunk 4*dt + x with x = 2*(g16&1) + (i16&3)/2, stored at (4*dt + x) ^ swz_v.
-    // With dt = 2*m + n that is 8*m + 4*(n ^ (sw >> 2)) + (x ^ (sw & 2)): two per-lane
-    // offsets (n = 0, 1) plus immediate offsets.
-    // voff(n) = vbase ^ (32*n): chunk bit 2 (n) is the only bit the two differ in.
+    // i.e. chunk 4*dt + x with x = 2*(g16&1) + (i16&3)/2 of quad dt, stored in quad
+    // dt ^ (swz_v / 4).  Element offset 32*(dt ^ s) + 8*x + 4*(i16&1) = vbase ^ (32*dt).
     const int vbase = [&] {
         const int vrow = 4 * hf + (i16 >> 2);  // row within each 16-row contraction
-        const int sw = swz_v(vrow);            // rows 16*c4 + vrow (+8) share it
+        const int sq = swz_v<D>(vrow) >> 2;    // rows 16*c4 + vrow (+8) share it
         const int x = 2 * (g16 & 1) + ((i16 & 3) >> 1);
-        return vrow * D + (4 * (sw >> 2) + (x ^ (sw & 2))) * 8 + 4 * (i16 & 1);
+        return vrow * D + 32 * sq + 8 * x + 4 * (i16 & 1);
     }();
     auto pv_part = [&](const bf16 *vt, const bf16x8 *pb, int c4) {
         int vb = vbase;
         asm volatile("" : "+v"(vb));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const bf16 *vp = vt + (vb ^ (32 * (dt & 1))) + 64 * (dt >> 1) + 16 * c4 * D;
+            const bf16 *vp = vt + (vb ^ (32 * dt)) + 16 * c4 * D;
             const bf16x4 lo = tr_read(vp);
             const bf16x4 hi = tr_read(vp + 8 * D);
             const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -327,16 +332,23 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         }
     };
 
-    // Raise the exponent reference to cover a new row maximum (raw units), lazily.
-    auto needs_rescale = [&](float mx) {
+    // Raise the exponent reference to cover a new row maximum (raw units), lazily: only
+    // when some row of the wave grew past R + kTau.  Returns the factor alpha that the
+    // running output must be multiplied by once the products issued under the old
+    // reference are done (1 when nothing changed); the row sum is rescaled here.
+    auto update_reference = [&](float mx, bool &changed) {
         m_nat = fmaxf(m_nat, mx * a.scale);
-        return __builtin_amdgcn_ballot_w64(mx * c > R + kTau) != 0;
+        changed = __builtin_amdgcn_ballot_w64(mx * c > R + kTau) != 0;
+        float alpha = 1.0f;
+        if (changed) {
+            const float Rn = fmaxf(R, mx * c);
+            alpha = __builtin_amdgcn_exp2f(R - Rn);  // R = -inf gives 0
+            R = Rn;
+            lsum *= alpha;
+        }
+        return alpha;
     };
-    auto rescale = [&](float mx) {
-        const float Rn = fmaxf(R, mx * c);
-        const float alpha = __builtin_amdgcn_exp2f(R - Rn);  // R = -inf gives 0
-        R = Rn;
-        lsum *= alpha;
+    auto rescale_output = [&](float alpha) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
     };
@@ -358,57 +370,54 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     {
         scores(K0, a.blk_rows - (int64_t)cS.tin * BC);
         cS.next(tiles_per_blk);
-        const float mx = row_max();
-        if (needs_rescale(mx)) rescale(mx);
+        bool changed;
+        const float alpha = update_reference(row_max(), changed);
+        if (changed) rescale_output(alpha);
 #pragma unroll
         for (int part = 0; part < 4; ++part) softmax_part(pp, part);
     }
     // Iteration 0 overwrites K buffer 0, which every wave has just read.
     __syncthreads();
 
-    // ---- main loop: iteration j = scores(j+1) + [PV(j) || softmax(j+1)].
-    // K(j+2) goes to the K buffer of tile j, V(j+1) to the V buffer of tile j-1.
+    // ---- main loop: iteration j = scores(j+1) + [PV(j) || softmax(j+1)], for every
+    // tile that has a successor.  K(j+2) goes to the K buffer of tile j, V(j+1) to the V
+    // buffer of tile j-1.
     auto iteration = [&](int32_t j, const bf16 *kcur, bf16 *knext, const bf16 *vcur,
                          bf16 *vnext) {
         if (j + 2 < n_tiles) {
             load_tile(Kh, cK, knext, koff_g, false);
             cK.next(tiles_per_blk);
         }
-        if (j + 1 < n_tiles) {
-            load_tile(Vh, cV, vnext, voff_g, true);
-            cV.next(tiles_per_blk);
-            scores(kcur, a.blk_rows - (int64_t)cS.tin * BC);
-            cS.next(tiles_per_blk);
-            const float mx = row_max();
-            // P(j+1) overwrites P(j) operand by operand, after the product using it.
-            if (needs_rescale(mx)) {
+        load_tile(Vh, cV, vnext, voff_g, true);
+        cV.next(tiles_per_blk);
+        scores(kcur, a.blk_rows - (int64_t)cS.tin * BC);
+        cS.next(tiles_per_blk);
+        bool changed;
+        const float alpha = update_reference(row_max(), changed);
+        // P(j) V(j) (old reference) interleaved with the numerators of tile j+1 (new
+        // reference); P(j+1) overwrites P(j) operand by operand after its product.
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    pv_part(vcur, pp, c4);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                rescale(mx);
-#pragma unroll
-                for (int part = 0; part < 4; ++part) softmax_part(pp, part);
-            } else {
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    pv_part(vcur, pp, c4);
-                    softmax_part(pp, c4);
-                    __builtin_amdgcn_sched_barrier(0);  // keep operand lifetimes per stage
-                }
-            }
-        } else {
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) pv_part(vcur, pp, c4);
+        for (int c4 = 0; c4 < 4; ++c4) {
+            pv_part(vcur, pp, c4);
+            softmax_part(pp, c4);
+            __builtin_amdgcn_sched_barrier(0);  // keep operand lifetimes per stage
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        if (changed) rescale_output(alpha);  // after the old-reference products
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
         __syncthreads();
     };
-    for (int32_t j = 0; j < n_tiles; j += 2) {
+    int32_t j = 0;
+    for (; j + 2 < n_tiles; j += 2) {  // tiles j and j+1 both have successors
         iteration(j, K1, K0, V0, V1);
-        if (j + 1 < n_tiles) iteration(j + 1, K0, K1, V1, V0);
+        iteration(j + 1, K0, K1, V1, V0);
     }
+    if (j + 1 < n_tiles) {
+        iteration(j, K1, K0, V0, V1);
+        ++j;
+    }
+    // Last tile: its P V product only.
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) pv_part((j & 1) ? V1 : V0, pp, c4);
 
     if constexpr (MODE == MODE_SHARE) {
         // The ring order the loads above followed, one entry per step.
