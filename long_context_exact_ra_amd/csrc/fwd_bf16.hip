@@ -22,18 +22,21 @@
 //    O^T = V^T P^T: no cross-lane shuffle of P.  The key order inside each
 //    16-deep contraction is permuted to match the score layout, and V^T is read
 //    from LDS with ds_read_b64_tr_b16 transpose loads using the same permutation.
-//  * Software pipeline inside each wave: iteration j computes the scores of tile
-//    j+1, then issues the P V products of tile j interleaved with the softmax
-//    (exp2, bf16 packing, row sums) of tile j+1, so matrix-core and vector-ALU work
-//    of one wave co-issue; the second wave on the SIMD fills the remaining gaps.
-//  * K and V tiles (64 keys) are double-buffered in LDS separately (K one tile
-//    ahead of V); the next tiles' global loads are issued at the top of an
-//    iteration and written to LDS at its end; one barrier per iteration.  Row
-//    pitches are padded against bank conflicts (K: +16 B for 16-byte row reads,
-//    V: +32 B for the 4-row transpose reads).
+//  * Software pipeline inside each wave, three tiles deep: A(t) = scores of tile t,
+//    B(t) = row max, exp2 and bf16 packing of tile t, C(t) = the P V products of
+//    tile t.  Iteration j runs A(j+2), C(j) and B(j+1) stage by stage (one 16-deep
+//    slice of each per stage), so the matrix-core work of one wave always has
+//    independent vector-ALU work beside it; the second wave on the SIMD fills the
+//    remaining gaps.
+//  * K and V tiles (64 keys) are double-buffered in LDS, K two tiles ahead of V.
+//    Each iteration starts the global loads of K(j+3) and V(j+1) straight into LDS
+//    (global_load_lds, no staging registers) and ends with one barrier.  Rows are
+//    stored unpadded with XOR swizzles of their 16-byte chunks, chosen so that both
+//    the 16-byte K fragment reads and the 4-row V transpose reads are free of bank
+//    conflicts.
 //  * The exponent reference is updated lazily: the O / l rescale only runs when
-//    some row's maximum grew by more than 2^kTau (a wave-uniform branch), so
-//    exp2(s*c - R) stays <= 2^kTau.  The true running maximum is tracked
+//    some row's scaled maximum (log2 units) passed the reference R by more than
+//    kTau (a wave-uniform branch), so exp2(s*c - R) stays <= 2^kTau.  The true running maximum is tracked
 //    separately and the state is converted to it at the end, so outputs obey
 //    m = exact running maximum.
 //  * Work-group ids are remapped so each XCD (8 per chip, one L2 each) works on a
@@ -51,9 +54,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BR = kBf16QueryTile;  // query rows per work-group
+constexpr int NW = 8;               // waves per work-group (32 query rows each)
+constexpr int BR = 32 * NW;         // query rows per work-group
 constexpr int BC = 64;              // keys per K/V tile
-constexpr int NT = 512;             // threads per work-group (8 waves)
+constexpr int NH = BC / 32;         // 32-key halves of a tile (one 32x32 score block each)
+constexpr int NSTAGE = 2 * NH;      // pipeline stages per tile = 16-key P V contractions
+constexpr int NT = 64 * NW;         // threads per work-group
 constexpr float kTau = 8.0f;        // lazy-rescale slack, in log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -97,11 +103,13 @@ struct TileCursor {
 
 template <int D>
 struct Tile {
-    static constexpr int CPR = D / 8;            // 16-byte chunks per row
-    static constexpr int RPL = 64 / CPR;         // rows filled by one wave-wide load
-    static constexpr int ROUND = RPL * (NT / 64);  // rows filled by one load of every wave
-    static constexpr int LOADS = BC / ROUND;     // loads per wave per tensor
-    static_assert(LOADS >= 1 && BC % ROUND == 0, "tile split");
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int RPL = 64 / CPR;              // rows filled by one wave-wide load
+    static constexpr int WAVE_LOADS = BC * CPR / 64;  // wave-wide loads per K or V tile
+    static constexpr int LOADERS = WAVE_LOADS < NW ? WAVE_LOADS : NW;  // waves that load
+    static constexpr int ROUND = RPL * LOADERS;       // rows filled by one load per loader
+    static constexpr int LOADS = BC / ROUND;          // loads per loading wave per tensor
+    static_assert(LOADS >= 1 && BC % ROUND == 0 && LOADS * LOADERS == WAVE_LOADS, "tile split");
 };
 
 // LDS tile layouts: rows of D bf16 without padding; the 16-byte chunk c of row r
@@ -122,6 +130,7 @@ template <int D, int MODE>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     using T = Tile<D>;
     constexpr int CPR = T::CPR, RPL = T::RPL, ROUND = T::ROUND, LOADS = T::LOADS;
+    constexpr int LOADERS = T::LOADERS;
     constexpr int NKK = D / 16;  // 16-deep contractions over the head dimension
     constexpr int NDT = D / 32;  // 32-wide output tiles over the head dimension
     constexpr int TILE = BC * D;  // elements per K or V tile
@@ -207,6 +216,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     const uint32_t voff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_v<D>(lrow)) * 8) * 2;
     auto load_tile = [&](const bf16 *base, const TileCursor &cur, bf16 *dst, uint32_t off,
                          bool is_v) {
+        if (LOADERS < NW && wave >= LOADERS) return;  // the tile needs fewer waves
         const int64_t row0 =
             ring_block(a.rank, cur.t, a.n_blocks) * a.blk_rows + (int64_t)cur.tin * BC;
         const int64_t left = a.blk_rows - (int64_t)cur.tin * BC;  // keys left in the block
@@ -241,10 +251,15 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         }
     };
 
-    // ---- S^T = K Q^T for one tile: lane = query, 16 keys per lane per 32-key half.
-    // s0[i] / s1[i] hold key 8*(i/4) + 4*hf + i%4 (+32 for s1) of the tile.
-    f32x16 s0, s1;
-    // K fragment addresses: row ln (and ln + 32, same swizzle), chunk (2*kk + hf) ^ sw.
+    // ---- S^T = K Q^T for one tile: lane = query, 16 keys per lane per 32-key block.
+    // sc.h[b][i] holds key 32*b + 8*(i/4) + 4*hf + i%4 of the tile.  Two score sets
+    // alternate: one is consumed by the softmax while the next tile's products
+    // accumulate into the other.
+    struct Scores {
+        f32x16 h[NH];
+    };
+    Scores sx, sy;
+    // K fragment addresses: row ln (+32*b, same swizzle), chunk (2*kk + hf) ^ sw.
     // Element offset 8*((2*kk + hf) ^ sw) = 16*(kk ^ (sw >> 1)) + 8*(hf ^ (sw & 1)), so
     // with kbase holding the sw terms the read for kk is at kbase ^ (16*kk): the kk bits
     // (4..6) are disjoint from the row and half bits.
@@ -252,56 +267,78 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         const int sw = swz_k<D>(ln);
         return ln * D + 8 * (hf ^ (sw & 1)) + 16 * (sw >> 1);
     }();
-    auto scores = [&](const bf16 *kt, int64_t nvalid) {
-        s0 = f32x16{};
-        s1 = f32x16{};
+    auto laundered_kbase = [&] {
         int kb = kbase;
-        asm volatile("" : "+v"(kb));  // derive the read offsets here, not kept live
+        asm volatile("" : "+v"(kb));  // derive the read offsets where used, not kept live
+        return kb;
+    };
+    constexpr int KK_STAGE = NKK / NSTAGE;  // contractions per pipeline stage
+    static_assert(KK_STAGE >= 1 && NKK % NSTAGE == 0, "stage split");
+    auto scores_stage = [&](const bf16 *kt, int kb, Scores &d, int stage) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
+        for (int u = 0; u < KK_STAGE; ++u) {
+            const int kk = stage * KK_STAGE + u;
             const bf16 *kp = kt + (kb ^ (16 * kk));
-            const bf16x8 k0 = *(const bf16x8 *)(kp);
-            const bf16x8 k1 = *(const bf16x8 *)(kp + 32 * D);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
-            if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
-        }
-        if (nvalid < BC) {
-            // key index = 8*(i/4) + i%4 + 4*hf: compare the constant part with a
-            // per-lane limit (no per-key registers).
-            const int lim = (int)nvalid - 4 * hf;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kc = 8 * (i >> 2) + (i & 3);
-                if (kc >= lim) s0[i] = -INFINITY;
-                if (kc + 32 >= lim) s1[i] = -INFINITY;
+            for (int b = 0; b < NH; ++b) {
+                const bf16x8 kf = *(const bf16x8 *)(kp + 32 * b * D);
+                d.h[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], d.h[b], 0, 0, 0);
             }
         }
     };
-
-    // Row max of the current scores (raw dot units), both lane halves combined.
-    auto row_max = [&]() {
-        float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s0[1], s1[1]);
+    auto zero_scores = [&](Scores &d) {
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) {
-            ma = fmaxf(fmaxf(ma, s0[i]), s1[i]);
-            mb = fmaxf(fmaxf(mb, s0[i + 1]), s1[i + 1]);
+        for (int b = 0; b < NH; ++b) d.h[b] = f32x16{};
+    };
+    auto scores_full = [&](const bf16 *kt, Scores &d) {
+        zero_scores(d);
+        const int kb = laundered_kbase();
+#pragma unroll
+        for (int stage = 0; stage < NSTAGE; ++stage) {
+            scores_stage(kt, kb, d, stage);
+            __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
         }
+    };
+    // Keys past the end of a partial tile get score -inf.
+    auto mask_scores = [&](Scores &d, int64_t nvalid) {
+        if (nvalid < BC) {
+            // key index = 32*b + 8*(i/4) + i%4 + 4*hf: compare the constant part with a
+            // per-lane limit (no per-key registers).
+            const int lim = (int)nvalid - 4 * hf;
+#pragma unroll
+            for (int b = 0; b < NH; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * b + 8 * (i >> 2) + (i & 3) >= lim) d.h[b][i] = -INFINITY;
+        }
+    };
+
+    // Row max of a score set (raw dot units), both lane halves combined.
+    auto row_max = [&](const Scores &d) {
+        float ma = d.h[0][0], mb = d.h[0][1];
+#pragma unroll
+        for (int b = 0; b < NH; ++b)
+#pragma unroll
+            for (int i = (b == 0 ? 2 : 0); i < 16; i += 4) {
+                ma = fmaxf(fmaxf(ma, d.h[b][i]), d.h[b][i + 2]);
+                mb = fmaxf(fmaxf(mb, d.h[b][i + 1]), d.h[b][i + 3]);
+            }
         const float mx = fmaxf(ma, mb);
         return fmaxf(mx, other_half(mx));
     };
 
-    // Softmax numerators of the current scores, packed into the four PV operands.
-    // Operand c4 covers keys 16*c4 + 8*(j/4) + 4*hf + j%4, j = 0..7.
+    // Softmax numerators of a score set, packed into the PV operands.  Operand c4
+    // covers keys 16*c4 + 8*(j/4) + 4*hf + j%4, j = 0..7, i.e. elements 8*(c4%2) + j of
+    // score block c4/2.
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    auto softmax_part = [&](bf16x8 *pb, int part) {
+    auto softmax_part = [&](const Scores &d, bf16x8 *pb, int part) {
         const float nR = -R;
+        const f32x16 &sv = d.h[part >> 1];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             const int i = 8 * (part & 1) + e;
-            const f32x16 &s = (part < 2) ? s0 : s1;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, nR));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, nR));
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c, nR));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i + 1], c, nR));
             const bf16x2 pk = {(bf16)p0, (bf16)p1};
             lsum = __builtin_amdgcn_fdot2_f32_bf16(ones, pk, lsum, false);
             pb[part][e] = pk[0];
@@ -353,8 +390,13 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
     };
 
-    // ---- prologue: K(0), K(1), V(0) into LDS; scores and softmax of tile 0.
-    TileCursor cK{0, 0}, cV{0, 0}, cS{0, 0};  // next K load, next V load, next scores
+    // Pipeline per tile t: A(t) scores, B(t) max + softmax, C(t) P V.  Iteration j
+    // runs A(j+2), B(j+1) and C(j), which are independent, stage by stage.
+    // Buffers: K(t) lives in K[t & 1], V(t) in V[t & 1]; S(t) in score set t & 1.
+    TileCursor cK{0, 0}, cV{0, 0}, cM{0, 0};  // next K load, next V load, next softmax
+    auto nvalid_of = [&](const TileCursor &cur) { return a.blk_rows - (int64_t)cur.tin * BC; };
+
+    // ---- prologue: K(0), K(1), V(0) into LDS; A(0), B(0), A(1); then K(2).
     load_tile(Kh, cK, K0, koff_g, false);
     cK.next(tiles_per_blk);
     load_tile(Vh, cV, V0, voff_g, true);
@@ -366,58 +408,88 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
     __syncthreads();
 
-    bf16x8 pp[4];  // packed softmax numerators of the tile whose P V product is next
+    bf16x8 pp[NSTAGE];  // packed softmax numerators of the tile whose P V product is next
     {
-        scores(K0, a.blk_rows - (int64_t)cS.tin * BC);
-        cS.next(tiles_per_blk);
+        scores_full(K0, sx);
+        mask_scores(sx, nvalid_of(cM));
+        cM.next(tiles_per_blk);
         bool changed;
-        const float alpha = update_reference(row_max(), changed);
+        const float alpha = update_reference(row_max(sx), changed);
         if (changed) rescale_output(alpha);
 #pragma unroll
-        for (int part = 0; part < 4; ++part) softmax_part(pp, part);
+        for (int part = 0; part < NSTAGE; ++part) softmax_part(sx, pp, part);
+        if (n_tiles > 1) scores_full(K1, sy);
     }
-    // Iteration 0 overwrites K buffer 0, which every wave has just read.
-    __syncthreads();
+    __syncthreads();  // every wave is done with K buffer 0
+    if (n_tiles > 2) {
+        load_tile(Kh, cK, K0, koff_g, false);
+        cK.next(tiles_per_blk);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    }
 
-    // ---- main loop: iteration j = scores(j+1) + [PV(j) || softmax(j+1)], for every
-    // tile that has a successor.  K(j+2) goes to the K buffer of tile j, V(j+1) to the V
-    // buffer of tile j-1.
-    auto iteration = [&](int32_t j, const bf16 *kcur, bf16 *knext, const bf16 *vcur,
-                         bf16 *vnext) {
-        if (j + 2 < n_tiles) {
+    // Iteration j with A(j+2): consumes S(j+1) from cs, accumulates S(j+2) into ns from
+    // K[j & 1], multiplies P(j) by V[j & 1]; loads K(j+3) into K[(j+1) & 1] and V(j+1)
+    // into V[(j+1) & 1].
+    auto full_iteration = [&](int32_t j, Scores &cs, Scores &ns, const bf16 *kcur, bf16 *knext,
+                              const bf16 *vcur, bf16 *vnext) {
+        if (j + 3 < n_tiles) {
             load_tile(Kh, cK, knext, koff_g, false);
             cK.next(tiles_per_blk);
         }
         load_tile(Vh, cV, vnext, voff_g, true);
         cV.next(tiles_per_blk);
-        scores(kcur, a.blk_rows - (int64_t)cS.tin * BC);
-        cS.next(tiles_per_blk);
+        mask_scores(cs, nvalid_of(cM));
+        cM.next(tiles_per_blk);
         bool changed;
-        const float alpha = update_reference(row_max(), changed);
-        // P(j) V(j) (old reference) interleaved with the numerators of tile j+1 (new
-        // reference); P(j+1) overwrites P(j) operand by operand after its product.
+        const float alpha = update_reference(row_max(cs), changed);
+        zero_scores(ns);
+        const int kb = laundered_kbase();
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            pv_part(vcur, pp, c4);
-            softmax_part(pp, c4);
-            __builtin_amdgcn_sched_barrier(0);  // keep operand lifetimes per stage
+        for (int stage = 0; stage < NSTAGE; ++stage) {
+            scores_stage(kcur, kb, ns, stage);
+            pv_part(vcur, pp, stage);
+            softmax_part(cs, pp, stage);  // P(j+1) replaces P(j) after its product
         }
         if (changed) rescale_output(alpha);  // after the old-reference products
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
         __syncthreads();
     };
+    // Iteration j without a next score tile (the last but one tile).
+    auto tail_iteration = [&](Scores &cs, const bf16 *vcur, bf16 *vnext) {
+        load_tile(Vh, cV, vnext, voff_g, true);
+        cV.next(tiles_per_blk);
+        mask_scores(cs, nvalid_of(cM));
+        cM.next(tiles_per_blk);
+        bool changed;
+        const float alpha = update_reference(row_max(cs), changed);
+#pragma unroll
+        for (int stage = 0; stage < NSTAGE; ++stage) {
+            pv_part(vcur, pp, stage);
+            softmax_part(cs, pp, stage);
+        }
+        if (changed) rescale_output(alpha);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    };
+
     int32_t j = 0;
-    for (; j + 2 < n_tiles; j += 2) {  // tiles j and j+1 both have successors
-        iteration(j, K1, K0, V0, V1);
-        iteration(j + 1, K0, K1, V1, V0);
+    for (; j + 3 < n_tiles; j += 2) {  // iterations j and j+1 both have a score stage
+        full_iteration(j, sy, sx, K0, K1, V0, V1);
+        full_iteration(j + 1, sx, sy, K1, K0, V1, V0);
+    }
+    if (j + 2 < n_tiles) {  // j even
+        full_iteration(j, sy, sx, K0, K1, V0, V1);
+        ++j;
     }
     if (j + 1 < n_tiles) {
-        iteration(j, K1, K0, V0, V1);
+        if (j & 1) tail_iteration(sx, V1, V0);
+        else tail_iteration(sy, V0, V1);
         ++j;
     }
     // Last tile: its P V product only.
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) pv_part((j & 1) ? V1 : V0, pp, c4);
+    for (int c4 = 0; c4 < NSTAGE; ++c4) pv_part((j & 1) ? V1 : V0, pp, c4);
 
     if constexpr (MODE == MODE_SHARE) {
         // The ring order the loads above followed, one entry per step.
@@ -473,6 +545,8 @@ hipError_t launch(const FwdArgs &a, hipStream_t st) {
 }
 
 }  // namespace
+
+int bf16_query_tile() { return BR; }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int B, int d, int mode, hipStream_t st) {
     (void)B;

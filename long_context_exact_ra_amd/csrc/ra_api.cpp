@@ -75,7 +75,7 @@ bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
 // Work-group count of the forward kernels; false if it does not fit a 1-D grid.
 bool grid_size(int32_t B, int32_t H, int64_t l_q, int32_t dtype, int32_t *n_qtiles,
                int32_t *n_wg) {
-    const int64_t tile = dtype == RA_BF16 ? ra::kBf16QueryTile : ra::kF32QueryTile;
+    const int64_t tile = dtype == RA_BF16 ? ra::bf16_query_tile() : ra::kF32QueryTile;
     const int64_t qt = (l_q + tile - 1) / tile;
     const int64_t total = qt * (int64_t)B * H;
     if (qt > INT32_MAX || total > INT32_MAX) return false;

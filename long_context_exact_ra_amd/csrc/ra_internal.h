@@ -44,7 +44,7 @@ enum Mode : int {
 };
 
 // Query rows per work-group of each kernel (the host sizes the grid with these).
-constexpr int kBf16QueryTile = 256;
+int bf16_query_tile();
 constexpr int kF32QueryTile = 64;
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int B, int d, int mode, hipStream_t st);
