@@ -30,6 +30,9 @@
  *  - Supported: d in {64, 128}; dtype RA_F32 or RA_BF16; scale finite and > 0;
  *    device pointers 16-byte aligned.  Any N >= 1 is allowed (the slowleelab page,
  *    pitfall 6, notes the ring works for any GPU count).
+ *  - With RA_BF16, one K (or V) head of the call, rows * d * 2 bytes, must stay
+ *    below 2^31 bytes (the kernel addresses a head through a 32-bit buffer range);
+ *    larger heads return RA_ENOTSUP.
  */
 #ifndef RA_H
 #define RA_H

@@ -30,7 +30,7 @@
 //    remaining gaps.
 //  * K and V tiles (64 keys) are double-buffered in LDS, K two tiles ahead of V.
 //    Each iteration starts the global loads of K(j+3) and V(j+1) straight into LDS
-//    (global_load_lds, no staging registers) and ends with one barrier.  Rows are
+//    (buffer loads with the LDS bit, no staging registers) and ends with one barrier.  Rows are
 //    stored unpadded with XOR swizzles of their 16-byte chunks, chosen so that both
 //    the 16-byte K fragment reads and the 4-row V transpose reads are free of bank
 //    conflicts.
@@ -62,6 +62,9 @@ constexpr int NSTAGE = 2 * NH;      // pipeline stages per tile = 16-key P V con
 constexpr int NT = 64 * NW;         // threads per work-group
 constexpr float kTau = 8.0f;        // lazy-rescale slack, in log2 units
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle, no thread-id addressing; reads past num_records return zero.
+constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ int xcd_remap(int wg, int n) {
     const int per = n / 8, rem = n % 8;
@@ -206,31 +209,36 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     const int32_t tiles_per_blk = (int32_t)((a.blk_rows + BC - 1) / BC);
     const int32_t n_tiles = tiles_per_blk * a.n_blocks;
 
-    // ---- direct global -> LDS tile loads (no staging registers).  Load p of wave w
-    // fills tile rows p*ROUND + w*RPL + lane/CPR; lane % CPR is the chunk slot.  One
-    // per-lane byte
+    // ---- direct global -> LDS tile loads (no staging registers), through buffer
+    // resources over this work-group's K and V heads.  The buffer form (rather than
+    // global_load_lds) keeps LDS reads countable in order: with a flat-encoded LDS DMA
+    // in flight every LDS wait degenerates to lgkmcnt(0), which serialises each matrix
+    // product behind the most recent fragment read.  Load p of wave w fills tile rows
+    // p*ROUND + w*RPL + lane/CPR; lane % CPR is the chunk slot.  One per-lane byte
     // offset per tensor serves every load (loads are ROUND >= 32 rows apart and the
-    // swizzles repeat every 16 rows); only the wave-uniform bases move.
+    // swizzles repeat every 16 rows); the row base goes in the scalar offset.
+    const int head_bytes = (int)((int64_t)a.n_blocks * a.blk_rows * (D * 2));  // host: < 2^31
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Kh, 0, head_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Vh, 0, head_bytes, kRsrcWord3);
     const int lrow = wave * RPL + lane / CPR;  // row of load 0
     const uint32_t koff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_k<D>(lrow)) * 8) * 2;
     const uint32_t voff_g = (uint32_t)(lrow * D + ((lane % CPR) ^ swz_v<D>(lrow)) * 8) * 2;
-    auto load_tile = [&](const bf16 *base, const TileCursor &cur, bf16 *dst, uint32_t off,
-                         bool is_v) {
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, const TileCursor &cur, bf16 *dst,
+                         uint32_t off, bool is_v) {
         if (LOADERS < NW && wave >= LOADERS) return;  // the tile needs fewer waves
         const int64_t row0 =
             ring_block(a.rank, cur.t, a.n_blocks) * a.blk_rows + (int64_t)cur.tin * BC;
         const int64_t left = a.blk_rows - (int64_t)cur.tin * BC;  // keys left in the block
-        const char *tile = (const char *)(base + row0 * D);  // wave-uniform
-        // Opaque per call, so the compiler keeps the offset 32-bit (SGPR base + VGPR
-        // offset addressing) instead of hoisting a 64-bit copy of it.
-        asm volatile("" : "+v"(off));
+        const uint32_t soff = (uint32_t)(row0 * (D * 2));           // wave-uniform
         bf16 *ldst = dst + wave * RPL * D;
         if (left >= BC) {
 #pragma unroll
             for (int p = 0; p < LOADS; ++p)
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(tile + (size_t)p * ROUND * D * 2 + off),
-                    (void __attribute__((address_space(3))) *)(ldst + p * ROUND * D), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (void __attribute__((address_space(3))) *)(ldst + p * ROUND * D), 16,
+                    (int)off, (int)(soff + (uint32_t)(p * ROUND * D * 2)), 0, 0);
         } else {
             // Ragged tail: rows past the block end repeat its last row; those keys are
             // masked, so their probabilities are exactly 0.
@@ -244,9 +252,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
                 const int r = p * ROUND + lr;
                 const int rr = r < last ? r : last;
                 const uint32_t o2 = (uint32_t)(rr * D + slot * 8) * 2;
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(tile + o2),
-                    (void __attribute__((address_space(3))) *)(ldst + p * ROUND * D), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (void __attribute__((address_space(3))) *)(ldst + p * ROUND * D), 16,
+                    (int)o2, (int)soff, 0, 0);
             }
         }
     };
@@ -397,12 +405,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     auto nvalid_of = [&](const TileCursor &cur) { return a.blk_rows - (int64_t)cur.tin * BC; };
 
     // ---- prologue: K(0), K(1), V(0) into LDS; A(0), B(0), A(1); then K(2).
-    load_tile(Kh, cK, K0, koff_g, false);
+    load_tile(krs, cK, K0, koff_g, false);
     cK.next(tiles_per_blk);
-    load_tile(Vh, cV, V0, voff_g, true);
+    load_tile(vrs, cV, V0, voff_g, true);
     cV.next(tiles_per_blk);
     if (n_tiles > 1) {
-        load_tile(Kh, cK, K1, koff_g, false);
+        load_tile(krs, cK, K1, koff_g, false);
         cK.next(tiles_per_blk);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     }
     __syncthreads();  // every wave is done with K buffer 0
     if (n_tiles > 2) {
-        load_tile(Kh, cK, K0, koff_g, false);
+        load_tile(krs, cK, K0, koff_g, false);
         cK.next(tiles_per_blk);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
@@ -434,10 +442,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     auto full_iteration = [&](int32_t j, Scores &cs, Scores &ns, const bf16 *kcur, bf16 *knext,
                               const bf16 *vcur, bf16 *vnext) {
         if (j + 3 < n_tiles) {
-            load_tile(Kh, cK, knext, koff_g, false);
+            load_tile(krs, cK, knext, koff_g, false);
             cK.next(tiles_per_blk);
         }
-        load_tile(Vh, cV, vnext, voff_g, true);
+        load_tile(vrs, cV, vnext, voff_g, true);
         cV.next(tiles_per_blk);
         mask_scores(cs, nvalid_of(cM));
         cM.next(tiles_per_blk);
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     };
     // Iteration j without a next score tile (the last but one tile).
     auto tail_iteration = [&](Scores &cs, const bf16 *vcur, bf16 *vnext) {
-        load_tile(Vh, cV, vnext, voff_g, true);
+        load_tile(vrs, cV, vnext, voff_g, true);
         cV.next(tiles_per_blk);
         mask_scores(cs, nvalid_of(cM));
         cM.next(tiles_per_blk);

@@ -72,6 +72,11 @@ bool heads_ok(int32_t B, int32_t H, int32_t H_kv, int32_t d, int32_t dtype) {
 
 bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
+// The bf16 kernel reads one K/V head through a buffer resource with a 32-bit range.
+bool head_range_ok(int32_t dtype, int64_t rows, int32_t d) {
+    return dtype != RA_BF16 || rows <= (int64_t)INT32_MAX / (2 * d);
+}
+
 // Work-group count of the forward kernels; false if it does not fit a 1-D grid.
 bool grid_size(int32_t B, int32_t H, int64_t l_q, int32_t dtype, int32_t *n_qtiles,
                int32_t *n_wg) {
@@ -139,6 +144,7 @@ int ra_step(const void *Q_i, const void *K_blk, const void *V_blk, float *O_acc,
     if (!ptr_ok(Q_i) || !ptr_ok(K_blk) || !ptr_ok(V_blk) || !ptr_ok(O_acc) || !ptr_ok(m) ||
         !ptr_ok(l))
         return RA_EINVAL;
+    if (!head_range_ok(s->dtype, s->l_kv, s->d)) return RA_ENOTSUP;
     ra::FwdArgs a{};
     if (!grid_size(s->B, s->H, s->l_q, s->dtype, &a.n_qtiles, &a.n_wg)) return RA_ENOTSUP;
     int rc = check_device();
@@ -187,6 +193,7 @@ int ra_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv
         !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast) ||
         (sched_trace != nullptr && ((uintptr_t)sched_trace & 3u) != 0))
         return RA_EINVAL;
+    if (!head_range_ok(dtype, L, d)) return RA_ENOTSUP;
     const int64_t l = L / N;
     ra::FwdArgs a{};
     if (!grid_size(B, H, l, dtype, &a.n_qtiles, &a.n_wg)) return RA_ENOTSUP;

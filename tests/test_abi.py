@@ -154,3 +154,11 @@ def test_binding_refuses_host_tensors():
     o = torch.zeros((1, 2, 4, 64))
     with pytest.raises(ValueError):
         ra.share_forward(0, 4, 16, 2, 2, 64, 1, q, k, k, 0.125, o)
+
+
+def test_bf16_heads_beyond_the_32_bit_buffer_range_are_unsupported():
+    # One bf16 K/V head of 2^23 rows x 128 dims is 2^31 bytes: past the kernel's
+    # 32-bit buffer range, refused before any device call.
+    assert _share(N=8, L=1 << 23, d=128) == ra.RA_ENOTSUP
+    assert _share(N=8, L=1 << 24, d=64) == ra.RA_ENOTSUP
+    assert _step(_shape(l_kv=1 << 23, kv_head_stride=0)) == ra.RA_ENOTSUP
