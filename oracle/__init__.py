@@ -16,6 +16,13 @@ attention_rows(...)
     The plain definition softmax(Q K^T * scale) V over a set of key ranges, fp64,
     every score materialised (C code in ra_oracle.c).  Returns the normalised
     output together with the row maximum M and the sum Z of exp(s - M).
+causal_share(...), token_positions(...), causal_pairs(...)
+    The causal share: a query attends only to keys at or before its own position in
+    the sequence (slowleelab page, 4.5 limitation 2 and 4.8), for three ways of
+    assigning tokens to ring members: contiguous blocks (the plain split of L2), the
+    striped (interleaved) assignment of Striped Attention (4.8), and the zigzag
+    assignment of two mirrored chunks per member (named in 4.5; the exact chunk
+    pairing is this package's reading, see token_positions).
 online_step(...)
     One merge of a K/V block into the running state (O_acc, m, l), in the order of
     the per-step pseudocode on the slowleelab page (section 4.3), fp64 numpy, with
@@ -65,6 +72,12 @@ def _load():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64, i64p, i64p,
             ctypes.c_int, f64p, f64p, f64p, ctypes.c_int]
+        lib.ra_oracle_rows_masked.restype = ctypes.c_int
+        lib.ra_oracle_rows_masked.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64, i64p, i64p,
+            ctypes.c_int, i64p, i64p, f64p, f64p, f64p, ctypes.c_int]
         lib.ra_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -103,13 +116,16 @@ def _raw(a: np.ndarray):
 
 
 def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
-                   rows=None, key_ranges=None, nthreads: int | None = None):
+                   rows=None, key_ranges=None, nthreads: int | None = None,
+                   qpos=None, kpos=None):
     """The plain definition over the listed key ranges, for the listed query rows.
 
     Q: [B, H, l_q, d]; K, V: [B, H_kv, L, d]; all float32, or all uint16 bf16 bits.
     rows: flat indices (b*H + h)*l_q + r (default: every row).
     key_ranges: list of (lo, hi) half-open key ranges (default: all L keys).
     scale: the fp32 scale the GPU uses, widened to fp64 here.
+    qpos, kpos: optional causal mask; key k is used for selected row i only if
+    kpos[k] <= qpos[i] (qpos has one entry per selected row, kpos one per key row).
     Returns (O [n, d] float64 normalised, M [n] float64, Z [n] float64).
     """
     dq, Qb = _raw(Q)
@@ -136,13 +152,23 @@ def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
         nthreads = max_threads()
     i64p = ctypes.POINTER(ctypes.c_int64)
     f64p = ctypes.POINTER(ctypes.c_double)
-    rc = _load().ra_oracle_rows(
+    if (qpos is None) != (kpos is None):
+        raise ValueError("qpos and kpos go together")
+    if qpos is not None:
+        qpos = np.ascontiguousarray(np.asarray(qpos, dtype=np.int64))
+        kpos = np.ascontiguousarray(np.asarray(kpos, dtype=np.int64))
+        if qpos.shape != (n,) or kpos.shape != (L,):
+            raise ValueError("qpos needs one entry per selected row, kpos one per key row")
+        qp, kp = qpos.ctypes.data_as(i64p), kpos.ctypes.data_as(i64p)
+    else:
+        qp = kp = None
+    rc = _load().ra_oracle_rows_masked(
         dq, Qb.ctypes.data, l_q, Kb.ctypes.data, Vb.ctypes.data, L, B, H, H_kv, d,
         float(scale), rows.ctypes.data_as(i64p), n, lo.ctypes.data_as(i64p),
-        hi.ctypes.data_as(i64p), len(key_ranges), O.ctypes.data_as(f64p),
+        hi.ctypes.data_as(i64p), len(key_ranges), qp, kp, O.ctypes.data_as(f64p),
         M.ctypes.data_as(f64p), Z.ctypes.data_as(f64p), int(nthreads))
     if rc != 0:
-        raise ValueError(f"ra_oracle_rows failed with code {rc}")
+        raise ValueError(f"ra_oracle_rows_masked failed with code {rc}")
     return O, M, Z
 
 
@@ -157,6 +183,77 @@ def share(Q, K, V, scale, rank: int, N: int, rows=None, steps: int | None = None
     order = ring_schedule(rank, N)[: (N if steps is None else steps)]
     ranges = [(j * l, (j + 1) * l) for j in order]
     return attention_rows(Q, K, V, scale, rows=rows, key_ranges=ranges, nthreads=nthreads)
+
+
+LAYOUTS = ("contiguous", "striped", "zigzag")
+
+
+def token_positions(layout: str, rank: int, N: int, l: int) -> np.ndarray:
+    """Global sequence positions of ring member `rank`'s l local tokens, in local order.
+
+    contiguous: the plain Ring Attention split, member i holds tokens i*l .. (i+1)*l-1
+                (slowleelab page, L2 problem statement: the sequence is split evenly
+                into N blocks, block i on GPU i).
+    striped:    Striped Attention's interleaved assignment (slowleelab page, 4.8):
+                member i holds tokens i, i+N, i+2N, ...; local token x is x*N + i.
+    zigzag:     the sequence is cut into 2N equal chunks of l/2 tokens and member i
+                holds chunk i followed by chunk 2N-1-i (reading of the "Zigzag Ring"
+                named in 4.5: each member pairs an early chunk with its mirror image,
+                which evens out causal work); l must be even.
+    """
+    if N < 1 or not 0 <= rank < N or l < 0:
+        raise ValueError("need N >= 1, 0 <= rank < N, l >= 0")
+    x = np.arange(l, dtype=np.int64)
+    if layout == "contiguous":
+        return rank * l + x
+    if layout == "striped":
+        return x * N + rank
+    if layout == "zigzag":
+        if l % 2:
+            raise ValueError("zigzag needs an even block length")
+        h = l // 2
+        return np.where(x < h, rank * h + x, (2 * N - 1 - rank) * h + (x - h))
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def layout_positions(layout: str, N: int, L: int) -> np.ndarray:
+    """Position of every row of a member-major [.., L, ..] tensor: row j*l + x holds
+    member j's local token x.  Gathering a sequence-ordered tensor with this index
+    gives the member-major layout a ring would hold."""
+    if L % N:
+        raise ValueError("L must split evenly into N blocks")
+    l = L // N
+    return np.concatenate([token_positions(layout, j, N, l) for j in range(N)])
+
+
+def causal_share(Q, K, V, scale, rank: int, N: int, layout: str, rows=None, nthreads=None):
+    """Rank `rank`'s causal share: every key of the whole sequence whose position is
+    at or before the query's own (slowleelab page, 4.5 limitation 2).
+
+    Q is the member's [B, H, l, d] block in local order; K and V are [B, H_kv, L, d] in
+    member-major layout (block j = member j's tokens, local order).  The visiting
+    order of the ring does not change the result, so all keys are listed at once.
+    """
+    B, H, l, d = Q.shape
+    L = K.shape[2]
+    if L != N * l:
+        raise ValueError("K/V must hold N blocks of the query block's length")
+    if rows is None:
+        rows = np.arange(B * H * l, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    qpos = token_positions(layout, rank, N, l)[rows % l]
+    kpos = layout_positions(layout, N, L)
+    return attention_rows(Q, K, V, scale, rows=rows, key_ranges=[(0, L)],
+                          nthreads=nthreads, qpos=qpos, kpos=kpos)
+
+
+def causal_pairs(rank: int, N: int, L: int, layout: str) -> int:
+    """Number of (query, key) pairs that member `rank`'s causal share evaluates for one
+    (batch, head): for each local query, the keys of the sequence at or before it."""
+    l = L // N
+    q = token_positions(layout, rank, N, l)
+    # positions 0..L-1 are each held once, so the keys at or before p number p + 1
+    return int(np.sum(q + 1))
 
 
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:

@@ -51,16 +51,28 @@ static double widen(const void *base, int dtype, int64_t idx)
     return (double)f;
 }
 
-/* Returns 0 on success, 1 on a bad argument, 2 on allocation failure. */
-int ra_oracle_rows(int dtype, const void *Q, int64_t l_q, const void *K, const void *V,
-                   int64_t L, int B, int H, int H_kv, int d, double scale,
-                   const int64_t *rows, int64_t n_rows, const int64_t *key_lo,
-                   const int64_t *key_hi, int n_ranges, double *O, double *M, double *Z,
-                   int nthreads)
+/*
+ * Causal masking (optional).  With qpos and kpos given, key k takes part in row i's
+ * softmax only if kpos[k] <= qpos[i]: a query attends to itself and to earlier
+ * tokens only (slowleelab page, 4.5 limitation 2: under causal attention the query
+ * block Q_i attends only to K blocks at or before it).  qpos[i] is the global
+ * sequence position of selected row i, kpos[k] that of key row k; the caller derives
+ * both from how tokens are assigned to ring members.  With both NULL every listed
+ * key is used.  A row left with no key is reported as an error (code 3).
+ *
+ * Returns 0 on success, 1 on a bad argument, 2 on allocation failure, 3 if a row has
+ * no admissible key.
+ */
+int ra_oracle_rows_masked(int dtype, const void *Q, int64_t l_q, const void *K,
+                          const void *V, int64_t L, int B, int H, int H_kv, int d,
+                          double scale, const int64_t *rows, int64_t n_rows,
+                          const int64_t *key_lo, const int64_t *key_hi, int n_ranges,
+                          const int64_t *qpos, const int64_t *kpos, double *O, double *M,
+                          double *Z, int nthreads)
 {
     if ((dtype != ORA_F32 && dtype != ORA_BF16) || !Q || !K || !V || !rows || !O || !M ||
         !Z || l_q < 1 || L < 1 || B < 1 || H < 1 || H_kv < 1 || d < 1 || H % H_kv != 0 ||
-        n_rows < 0 || n_ranges < 1 || !key_lo || !key_hi)
+        n_rows < 0 || n_ranges < 1 || !key_lo || !key_hi || (!qpos) != (!kpos))
         return 1;
     int64_t n_keys = 0;
     for (int i = 0; i < n_ranges; i++) {
@@ -85,7 +97,7 @@ int ra_oracle_rows(int dtype, const void *Q, int64_t l_q, const void *K, const v
         double *acc = (double *)malloc(sizeof(double) * (size_t)d);
         if (!q || !s || !acc) {
 #pragma omp atomic write
-            failed = 1;
+            failed = 2;
         }
 #pragma omp for schedule(dynamic, 1)
         for (int64_t i = 0; i < n_rows; i++) {
@@ -103,15 +115,22 @@ int ra_oracle_rows(int dtype, const void *Q, int64_t l_q, const void *K, const v
             for (int c = 0; c < d; c++)
                 q[c] = widen(Q, dtype, q_base + c);
 
-            /* scores of every listed key */
+            /* scores of every listed, admissible key */
             int64_t n = 0;
             for (int rg = 0; rg < n_ranges; rg++)
                 for (int64_t k = key_lo[rg]; k < key_hi[rg]; k++) {
+                    if (qpos && kpos[k] > qpos[i])
+                        continue;
                     double dot = 0.0;
                     for (int c = 0; c < d; c++)
                         dot += q[c] * widen(K, dtype, kv_base + k * d + c);
                     s[n++] = scale * dot;
                 }
+            if (n == 0) {
+#pragma omp atomic write
+                failed = 3;
+                continue;
+            }
             /* safe softmax: maximum, shifted exponentials, their sum */
             double mx = s[0];
             for (int64_t k = 1; k < n; k++)
@@ -128,6 +147,8 @@ int ra_oracle_rows(int dtype, const void *Q, int64_t l_q, const void *K, const v
             n = 0;
             for (int rg = 0; rg < n_ranges; rg++)
                 for (int64_t k = key_lo[rg]; k < key_hi[rg]; k++) {
+                    if (qpos && kpos[k] > qpos[i])
+                        continue;
                     const double p = s[n++];
                     for (int c = 0; c < d; c++)
                         acc[c] += p * widen(V, dtype, kv_base + k * d + c);
@@ -141,7 +162,18 @@ int ra_oracle_rows(int dtype, const void *Q, int64_t l_q, const void *K, const v
         free(s);
         free(acc);
     }
-    return failed ? 2 : 0;
+    return failed;
+}
+
+/* Unmasked form: every listed key of every selected row. */
+int ra_oracle_rows(int dtype, const void *Q, int64_t l_q, const void *K, const void *V,
+                   int64_t L, int B, int H, int H_kv, int d, double scale,
+                   const int64_t *rows, int64_t n_rows, const int64_t *key_lo,
+                   const int64_t *key_hi, int n_ranges, double *O, double *M, double *Z,
+                   int nthreads)
+{
+    return ra_oracle_rows_masked(dtype, Q, l_q, K, V, L, B, H, H_kv, d, scale, rows, n_rows,
+                                 key_lo, key_hi, n_ranges, NULL, NULL, O, M, Z, nthreads);
 }
 
 /* Thread count the OpenMP runtime would use by default (for reporting). */
