@@ -150,6 +150,51 @@ int ra_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv
                      const void *V, float scale, float *O, float *m_out, float *l_out,
                      void *O_cast, int32_t *sched_trace, void *stream);
 
+/*
+ * How the tokens of the sequence are assigned to ring members, for the causal share.
+ * Member r holds l = L / N tokens; its local token x sits at global position
+ *   RA_LAYOUT_CONTIGUOUS  r*l + x                       (the plain split of the
+ *                         sequence into N consecutive blocks, slowleelab page, L2)
+ *   RA_LAYOUT_STRIPED     x*N + r                       (Striped Attention's
+ *                         interleaved assignment, slowleelab page, 4.8)
+ *   RA_LAYOUT_ZIGZAG      with h = l/2: r*h + x for x < h, (2N-1-r)*h + (x-h) after:
+ *                         chunks r and 2N-1-r of 2N equal chunks (the zigzag ring
+ *                         named in 4.5; this chunk pairing is the library's reading)
+ */
+typedef enum ra_layout {
+    RA_LAYOUT_CONTIGUOUS = 0,
+    RA_LAYOUT_STRIPED = 1,
+    RA_LAYOUT_ZIGZAG = 2
+} ra_layout;
+
+/*
+ * Causal share of ring member `rank` in one launch (slowleelab page, 4.5 limitation 2:
+ * under causal attention a query may only attend to keys at or before its own
+ * position).  Same computation as ra_share_forward except that a key enters a query's
+ * softmax only if its global position (per `layout`) is <= the query's.  Q_i holds the
+ * member's tokens in local order; K and V hold the whole sequence in member-major
+ * order: rows j*l .. (j+1)*l - 1 are member j's tokens, local order.
+ * Key tiles with no admissible key for any query of a work-group are skipped, so the
+ * work follows the layout: growing with the rank for RA_LAYOUT_CONTIGUOUS (the 50 %
+ * waste of 4.5), nearly equal across members for the striped and zigzag layouts.
+ * Every query has at least one admissible key (itself), so the output is defined.
+ *   layout   an ra_layout; RA_LAYOUT_ZIGZAG needs l to be a multiple of 128 (each
+ *            half-block a whole number of 64-key tiles), else RA_EINVAL
+ *   O, m_out, l_out, O_cast as in ra_share_forward (m and l over admissible keys).
+ * L == 0 is a no-op.  Other arguments and errors as in ra_share_forward.
+ */
+int ra_causal_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                            int32_t d, int32_t B, int32_t dtype, int32_t layout,
+                            const void *Q_i, const void *K, const void *V, float scale,
+                            float *O, float *m_out, float *l_out, void *O_cast, void *stream);
+
+/*
+ * Number of (query, key) pairs member `rank`'s causal share evaluates per (batch,
+ * head): the sum over its queries of the keys at or before each.  Host only; exact.
+ * Returns -RA_EINVAL for bad N, rank, L (L % N != 0, L < 0) or layout (zigzag: odd l).
+ */
+int64_t ra_causal_pairs(int32_t rank, int32_t N, int64_t L, int32_t layout);
+
 /* Static description of a status code. */
 const char *ra_strerror(int status);
 

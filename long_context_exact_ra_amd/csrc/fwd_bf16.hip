@@ -65,6 +65,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format,
 // no swizzle, no thread-id addressing; reads past num_records return zero.
 constexpr int kRsrcWord3 = 0x00020000;
+// Token layouts of a causal share (values of the public ra_layout).
+constexpr int32_t RA_LAYOUT_CONTIGUOUS_ = 0;
+constexpr int32_t RA_LAYOUT_STRIPED_ = 1;
 
 __device__ __forceinline__ int xcd_remap(int wg, int n) {
     const int per = n / 8, rem = n % 8;
@@ -93,14 +96,60 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16 *p) {
 }
 
 // Position of one K/V tile in the ring walk, advanced without divisions.
+// Blocks may contribute fewer tiles than they hold (a causal share skips key tiles
+// that no query of the work-group may attend to); act is the number of tiles of the
+// current block that are visited, always a prefix of the block.
 struct TileCursor {
     int32_t t;    // ring step
     int32_t tin;  // tile index inside the block
-    __device__ __forceinline__ void next(int32_t tiles_per_blk) {
-        if (++tin == tiles_per_blk) {
+    int32_t act;  // tiles of block j(t) that are visited
+    template <typename ActOf>
+    __device__ __forceinline__ void next(const ActOf &act_of, int32_t n_blocks) {
+        if (++tin == act) {
             tin = 0;
-            ++t;
+            do {
+                ++t;
+                act = t < n_blocks ? act_of(t) : 0;
+            } while (t < n_blocks && act == 0);
         }
+    }
+};
+
+// Causal mask of a share (slowleelab "Ring Attention" page, 4.5 limitation 2: a query
+// attends only to keys at or before its own position).  Member r's local token x sits
+// at position r*l + x (contiguous), x*N + r (striped) or, with h = l/2, r*h + x for
+// x < h and (2N-1-r)*h + (x-h) after (zigzag).  allowed(a, j, b0) is the number of keys
+// b0, b0+1, ... of block j that local query a may attend to (any sign; only its
+// clamp to [0, 64] matters).  A 64-key tile never straddles a zigzag half-block.
+struct CausalMap {
+    int32_t layout, rank, N, l;
+    __device__ __forceinline__ int32_t qpos(int32_t a) const {  // contiguous and zigzag
+        if (layout == RA_LAYOUT_CONTIGUOUS_) return rank * l + a;
+        const int32_t hl = l >> 1;
+        return a < hl ? rank * hl + a : (2 * N - 1 - rank) * hl + (a - hl);
+    }
+    __device__ __forceinline__ int32_t kpos(int32_t j, int32_t b) const {
+        if (layout == RA_LAYOUT_CONTIGUOUS_) return j * l + b;
+        const int32_t hl = l >> 1;
+        return b < hl ? j * hl + b : (2 * N - 1 - j) * hl + (b - hl);
+    }
+    __device__ __forceinline__ int32_t allowed(int32_t a, int32_t j, int32_t b0) const {
+        // striped: x*N + j <= a*N + r  <=>  x <= a - (j > r)
+        if (layout == RA_LAYOUT_STRIPED_) return a - (j > rank ? 1 : 0) - b0 + 1;
+        return qpos(a) - kpos(j, b0) + 1;
+    }
+    // Tiles of block j that hold a key some query up to local index a_max may attend to.
+    __device__ __forceinline__ int32_t active_tiles(int32_t j, int32_t a_max,
+                                                    int32_t tiles_per_blk) const {
+        auto prefix = [](int32_t keys, int32_t cap) {  // tiles covering keys 0..keys-1
+            return keys <= 0 ? 0 : min(cap, (keys + BC - 1) / BC);
+        };
+        if (layout == RA_LAYOUT_STRIPED_)
+            return prefix(a_max - (j > rank ? 1 : 0) + 1, tiles_per_blk);
+        const int32_t q = qpos(a_max);  // positions grow with the local index
+        if (layout == RA_LAYOUT_CONTIGUOUS_) return prefix(q - j * l + 1, tiles_per_blk);
+        const int32_t hl = l >> 1, ht = hl / BC;
+        return prefix(q - j * hl + 1, ht) + prefix(q - (2 * N - 1 - j) * hl + 1, ht);
     }
 };
 
@@ -129,7 +178,7 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-template <int D, int MODE>
+template <int D, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     using T = Tile<D>;
     constexpr int CPR = T::CPR, RPL = T::RPL, ROUND = T::ROUND, LOADS = T::LOADS;
@@ -152,7 +201,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     // Work-group coordinates are uniform; integer division would otherwise leave them
     // in VGPRs.
     const int wg = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, a.n_wg));
-    const int qt = __builtin_amdgcn_readfirstlane(wg % a.n_qtiles);
+    // A causal share gives later query tiles more keys: start those first.
+    const int qt = __builtin_amdgcn_readfirstlane(
+        CAUSAL ? a.n_qtiles - 1 - wg % a.n_qtiles : wg % a.n_qtiles);
     const int bh = __builtin_amdgcn_readfirstlane(wg / a.n_qtiles);
     const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
     const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
@@ -207,7 +258,20 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     const float c = a.scale_log2;
     // The host guarantees the tile count of a launch fits in int32.
     const int32_t tiles_per_blk = (int32_t)((a.blk_rows + BC - 1) / BC);
-    const int32_t n_tiles = tiles_per_blk * a.n_blocks;
+    const CausalMap cmap{a.layout, a.rank, a.n_blocks, (int32_t)a.blk_rows};
+    // Last valid local query of the work-group (uniform); positions grow with it.
+    const int64_t a_end = (int64_t)(qt + 1) * BR;
+    const int32_t a_max = (int32_t)((a.l_q < a_end ? a.l_q : a_end) - 1);
+    auto act_of = [&](int32_t t) -> int32_t {
+        if constexpr (!CAUSAL) return tiles_per_blk;
+        else return cmap.active_tiles((int32_t)ring_block(a.rank, t, a.n_blocks), a_max,
+                                      tiles_per_blk);
+    };
+    int32_t n_tiles = tiles_per_blk * a.n_blocks;
+    if constexpr (CAUSAL) {
+        n_tiles = 0;
+        for (int32_t t = 0; t < a.n_blocks; ++t) n_tiles += act_of(t);
+    }
 
     // ---- direct global -> LDS tile loads (no staging registers), through buffer
     // resources over this work-group's K and V heads.  The buffer form (rather than
@@ -307,12 +371,22 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
         }
     };
-    // Keys past the end of a partial tile get score -inf.
-    auto mask_scores = [&](Scores &d, int64_t nvalid) {
-        if (nvalid < BC) {
+    // Keys past the end of a partial tile, and keys a causal share may not attend to,
+    // get score -inf.
+    const int32_t a_lane = qt * BR + qloc;  // this lane's local query index
+    auto mask_scores = [&](Scores &d, const TileCursor &cur) {
+        const int64_t nvalid = a.blk_rows - (int64_t)cur.tin * BC;
+        int keys = nvalid < BC ? (int)nvalid : BC;  // admissible prefix of the tile
+        bool partial = keys < BC;
+        if constexpr (CAUSAL) {
+            const int32_t j = (int32_t)ring_block(a.rank, cur.t, a.n_blocks);
+            keys = min(keys, max(cmap.allowed(a_lane, j, cur.tin * BC), 0));
+            partial = __builtin_amdgcn_ballot_w64(keys < BC) != 0;  // wave-uniform
+        }
+        if (partial) {
             // key index = 32*b + 8*(i/4) + i%4 + 4*hf: compare the constant part with a
             // per-lane limit (no per-key registers).
-            const int lim = (int)nvalid - 4 * hf;
+            const int lim = keys - 4 * hf;
 #pragma unroll
             for (int b = 0; b < NH; ++b)
 #pragma unroll
@@ -401,17 +475,17 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     // Pipeline per tile t: A(t) scores, B(t) max + softmax, C(t) P V.  Iteration j
     // runs A(j+2), B(j+1) and C(j), which are independent, stage by stage.
     // Buffers: K(t) lives in K[t & 1], V(t) in V[t & 1]; S(t) in score set t & 1.
-    TileCursor cK{0, 0}, cV{0, 0}, cM{0, 0};  // next K load, next V load, next softmax
-    auto nvalid_of = [&](const TileCursor &cur) { return a.blk_rows - (int64_t)cur.tin * BC; };
+    const int32_t act0 = act_of(0);  // the member's own block: its first tile always counts
+    TileCursor cK{0, 0, act0}, cV{0, 0, act0}, cM{0, 0, act0};  // next K/V load, next softmax
 
     // ---- prologue: K(0), K(1), V(0) into LDS; A(0), B(0), A(1); then K(2).
     load_tile(krs, cK, K0, koff_g, false);
-    cK.next(tiles_per_blk);
+    cK.next(act_of, a.n_blocks);
     load_tile(vrs, cV, V0, voff_g, true);
-    cV.next(tiles_per_blk);
+    cV.next(act_of, a.n_blocks);
     if (n_tiles > 1) {
         load_tile(krs, cK, K1, koff_g, false);
-        cK.next(tiles_per_blk);
+        cK.next(act_of, a.n_blocks);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
     __syncthreads();
@@ -419,8 +493,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     bf16x8 pp[NSTAGE];  // packed softmax numerators of the tile whose P V product is next
     {
         scores_full(K0, sx);
-        mask_scores(sx, nvalid_of(cM));
-        cM.next(tiles_per_blk);
+        mask_scores(sx, cM);
+        cM.next(act_of, a.n_blocks);
         bool changed;
         const float alpha = update_reference(row_max(sx), changed);
         if (changed) rescale_output(alpha);
@@ -431,7 +505,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();  // every wave is done with K buffer 0
     if (n_tiles > 2) {
         load_tile(krs, cK, K0, koff_g, false);
-        cK.next(tiles_per_blk);
+        cK.next(act_of, a.n_blocks);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
@@ -443,12 +517,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
                               const bf16 *vcur, bf16 *vnext) {
         if (j + 3 < n_tiles) {
             load_tile(krs, cK, knext, koff_g, false);
-            cK.next(tiles_per_blk);
+            cK.next(act_of, a.n_blocks);
         }
         load_tile(vrs, cV, vnext, voff_g, true);
-        cV.next(tiles_per_blk);
-        mask_scores(cs, nvalid_of(cM));
-        cM.next(tiles_per_blk);
+        cV.next(act_of, a.n_blocks);
+        mask_scores(cs, cM);
+        cM.next(act_of, a.n_blocks);
         bool changed;
         const float alpha = update_reference(row_max(cs), changed);
         zero_scores(ns);
@@ -466,9 +540,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     // Iteration j without a next score tile (the last but one tile).
     auto tail_iteration = [&](Scores &cs, const bf16 *vcur, bf16 *vnext) {
         load_tile(vrs, cV, vnext, voff_g, true);
-        cV.next(tiles_per_blk);
-        mask_scores(cs, nvalid_of(cM));
-        cM.next(tiles_per_blk);
+        cV.next(act_of, a.n_blocks);
+        mask_scores(cs, cM);
+        cM.next(act_of, a.n_blocks);
         bool changed;
         const float alpha = update_reference(row_max(cs), changed);
 #pragma unroll
@@ -546,9 +620,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool CAUSAL = false>
 hipError_t launch(const FwdArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE>), dim3(a.n_wg), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, CAUSAL>), dim3(a.n_wg), dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 
@@ -558,6 +632,12 @@ int bf16_query_tile() { return BR; }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int B, int d, int mode, hipStream_t st) {
     (void)B;
+    if (a.layout != kNoCausal) {  // causal shares only
+        if (mode != MODE_SHARE) return hipErrorInvalidValue;
+        if (d == 128) return launch<128, MODE_SHARE, true>(a, st);
+        if (d == 64) return launch<64, MODE_SHARE, true>(a, st);
+        return hipErrorInvalidValue;
+    }
     if (d == 128) return mode == MODE_SHARE ? launch<128, MODE_SHARE>(a, st)
                                             : launch<128, MODE_STEP>(a, st);
     if (d == 64) return mode == MODE_SHARE ? launch<64, MODE_SHARE>(a, st)

@@ -16,7 +16,19 @@ constexpr int BC = 32;             // keys per tile
 constexpr int NT = 256;            // 4 lanes per query row
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D, int MODE>
+// Global sequence position of local token x of ring member `member` under a causal
+// share's token layout: contiguous r*l + x, striped x*N + r, zigzag (h = l/2) r*h + x
+// for x < h and (2N-1-r)*h + (x-h) after (slowleelab "Ring Attention" page, 4.5 and
+// 4.8).  A key is admissible for a query when its position is not later.
+__device__ __forceinline__ int64_t token_position(int32_t layout, int64_t member, int64_t N,
+                                                  int64_t l, int64_t x) {
+    if (layout == 0) return member * l + x;
+    if (layout == 1) return x * N + member;
+    const int64_t h = l / 2;
+    return x < h ? member * h + x : (2 * N - 1 - member) * h + (x - h);
+}
+
+template <int D, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdArgs a) {
     constexpr int DL = D / 4;  // head-dim elements per lane
     __shared__ float Ks[BC * D];
@@ -51,6 +63,8 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdArgs a) {
         }
     }
     const float c = a.scale_log2;
+    const int64_t qpos =
+        CAUSAL ? token_position(a.layout, a.rank, a.n_blocks, a.blk_rows, q) : 0;
     const int64_t tiles_per_blk = (a.blk_rows + BC - 1) / BC;
     const int64_t n_tiles = tiles_per_blk * a.n_blocks;
 
@@ -83,7 +97,11 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdArgs a) {
                 part_dot = __builtin_fmaf(qv[jj], Ks[k * D + 4 * jj + part], part_dot);
             part_dot += __shfl_xor(part_dot, 1);
             part_dot += __shfl_xor(part_dot, 2);
-            s[k] = (k < nvalid) ? part_dot : -INFINITY;
+            bool keep = k < nvalid;
+            if constexpr (CAUSAL)
+                keep = keep && token_position(a.layout, j, a.n_blocks, a.blk_rows,
+                                              tin * BC + k) <= qpos;
+            s[k] = keep ? part_dot : -INFINITY;
             mx = fmaxf(mx, s[k]);
         }
         m_nat = fmaxf(m_nat, mx * a.scale);
@@ -124,9 +142,9 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdArgs a) {
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool CAUSAL = false>
 hipError_t launch(const FwdArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_f32_kernel<D, MODE>), dim3(a.n_wg), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, MODE, CAUSAL>), dim3(a.n_wg), dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 
@@ -134,6 +152,12 @@ hipError_t launch(const FwdArgs &a, hipStream_t st) {
 
 hipError_t launch_fwd_f32(const FwdArgs &a, int B, int d, int mode, hipStream_t st) {
     (void)B;
+    if (a.layout != kNoCausal) {  // causal shares only
+        if (mode != MODE_SHARE) return hipErrorInvalidValue;
+        if (d == 128) return launch<128, MODE_SHARE, true>(a, st);
+        if (d == 64) return launch<64, MODE_SHARE, true>(a, st);
+        return hipErrorInvalidValue;
+    }
     if (d == 128) return mode == MODE_SHARE ? launch<128, MODE_SHARE>(a, st)
                                             : launch<128, MODE_STEP>(a, st);
     if (d == 64) return mode == MODE_SHARE ? launch<64, MODE_SHARE>(a, st)

@@ -96,6 +96,47 @@ int launch_fwd(const ra::FwdArgs &a, int32_t B, int32_t d, int32_t dtype, int mo
     return after_launch(e, st);
 }
 
+int share_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, int32_t d,
+                 int32_t B, int32_t dtype, int32_t layout, const void *Q_i, const void *K,
+                 const void *V, float scale, float *O, float *m_out, float *l_out,
+                 void *O_cast, int32_t *sched_trace, void *stream) {
+    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
+        !heads_ok(B, H, H_kv, d, dtype) || !scale_ok(scale))
+        return RA_EINVAL;
+    if (L == 0) return RA_OK;
+    if (!ptr_ok(Q_i) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(O) || !opt_ptr_ok(m_out) ||
+        !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast) ||
+        (sched_trace != nullptr && ((uintptr_t)sched_trace & 3u) != 0))
+        return RA_EINVAL;
+    if (!head_range_ok(dtype, L, d)) return RA_ENOTSUP;
+    const int64_t l = L / N;
+    ra::FwdArgs a{};
+    if (!grid_size(B, H, l, dtype, &a.n_qtiles, &a.n_wg)) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    a.Q = Q_i;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.m = m_out;
+    a.l = l_out;
+    a.O_cast = O_cast;
+    a.trace = sched_trace;
+    a.l_q = l;
+    a.blk_rows = l;
+    a.kv_head_stride = L * d;
+    a.kv_batch_stride = (int64_t)H_kv * L * d;
+    a.n_blocks = N;
+    a.rank = rank;
+    a.H = H;
+    a.H_kv = H_kv;
+    a.group = H / H_kv;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.layout = layout;
+    return launch_fwd(a, B, d, dtype, ra::MODE_SHARE, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,6 +202,7 @@ int ra_step(const void *Q_i, const void *K_blk, const void *V_blk, float *O_acc,
     a.kv_batch_stride = bs;
     a.n_blocks = 1;
     a.rank = 0;
+    a.layout = ra::kNoCausal;
     a.H = s->H;
     a.H_kv = s->H_kv;
     a.group = s->H / s->H_kv;
@@ -185,40 +227,41 @@ int ra_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv
                      int32_t d, int32_t B, int32_t dtype, const void *Q_i, const void *K,
                      const void *V, float scale, float *O, float *m_out, float *l_out,
                      void *O_cast, int32_t *sched_trace, void *stream) {
-    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
-        !heads_ok(B, H, H_kv, d, dtype) || !scale_ok(scale))
+    return share_launch(rank, N, L, H, H_kv, d, B, dtype, ra::kNoCausal, Q_i, K, V, scale, O,
+                        m_out, l_out, O_cast, sched_trace, stream);
+}
+
+int ra_causal_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                            int32_t d, int32_t B, int32_t dtype, int32_t layout,
+                            const void *Q_i, const void *K, const void *V, float scale,
+                            float *O, float *m_out, float *l_out, void *O_cast, void *stream) {
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED &&
+        layout != RA_LAYOUT_ZIGZAG)
         return RA_EINVAL;
-    if (L == 0) return RA_OK;
-    if (!ptr_ok(Q_i) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(O) || !opt_ptr_ok(m_out) ||
-        !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast) ||
-        (sched_trace != nullptr && ((uintptr_t)sched_trace & 3u) != 0))
+    // Zigzag: each half-block must be whole 64-key tiles, so no key tile straddles the
+    // two chunks a member holds.
+    if (layout == RA_LAYOUT_ZIGZAG && N >= 1 && L >= 0 && L % N == 0 && (L / N) % 128 != 0)
         return RA_EINVAL;
-    if (!head_range_ok(dtype, L, d)) return RA_ENOTSUP;
-    const int64_t l = L / N;
-    ra::FwdArgs a{};
-    if (!grid_size(B, H, l, dtype, &a.n_qtiles, &a.n_wg)) return RA_ENOTSUP;
-    int rc = check_device();
-    if (rc != RA_OK) return rc;
-    a.Q = Q_i;
-    a.K = K;
-    a.V = V;
-    a.O = O;
-    a.m = m_out;
-    a.l = l_out;
-    a.O_cast = O_cast;
-    a.trace = sched_trace;
-    a.l_q = l;
-    a.blk_rows = l;
-    a.kv_head_stride = L * d;
-    a.kv_batch_stride = (int64_t)H_kv * L * d;
-    a.n_blocks = N;
-    a.rank = rank;
-    a.H = H;
-    a.H_kv = H_kv;
-    a.group = H / H_kv;
-    a.scale = scale;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    return launch_fwd(a, B, d, dtype, ra::MODE_SHARE, (hipStream_t)stream);
+    return share_launch(rank, N, L, H, H_kv, d, B, dtype, layout, Q_i, K, V, scale, O, m_out,
+                        l_out, O_cast, nullptr, stream);
+}
+
+int64_t ra_causal_pairs(int32_t rank, int32_t N, int64_t L, int32_t layout) {
+    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0) return -RA_EINVAL;
+    const int64_t l = L / N, r = rank;
+    switch (layout) {
+    case RA_LAYOUT_CONTIGUOUS:  // queries r*l + x see r*l + x + 1 keys
+        return l * r * l + l * (l + 1) / 2;
+    case RA_LAYOUT_STRIPED:  // queries x*N + r see x*N + r + 1 keys
+        return (int64_t)N * (l * (l - 1) / 2) + l * (r + 1);
+    case RA_LAYOUT_ZIGZAG: {  // chunk r then chunk 2N-1-r, h tokens each
+        if (l % 2) return -RA_EINVAL;
+        const int64_t h = l / 2;
+        return h * (r * h) + h * (h + 1) / 2 + h * ((2 * (int64_t)N - 1 - r) * h) +
+               h * (h + 1) / 2;
+    }
+    default: return -RA_EINVAL;
+    }
 }
 
 const char *ra_strerror(int status) {

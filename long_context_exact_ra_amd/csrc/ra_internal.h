@@ -36,7 +36,10 @@ struct FwdArgs {
     int32_t n_wg;      // total work-groups of the launch
     float scale;       // score scale (normally 1/sqrt(d))
     float scale_log2;  // scale * log2(e): exponentials are taken as exp2
+    int32_t layout;    // causal token layout (ra_layout), or kNoCausal
 };
+
+constexpr int32_t kNoCausal = -1;
 
 enum Mode : int {
     MODE_SHARE = 0,  // no state in; finalised output out

@@ -16,6 +16,9 @@ import torch
 
 RA_OK, RA_EINVAL, RA_ENOTSUP, RA_EHIP = 0, 1, 2, 3
 RA_F32, RA_BF16 = 0, 1
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
+LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED,
+           "zigzag": RA_LAYOUT_ZIGZAG}
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
 _lib = None
@@ -62,6 +65,10 @@ def load():
         "ra_finalize": (ctypes.c_int, [vp, vp, shp, vp, vp]),
         "ra_share_forward": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, i32, vp, vp,
                                             vp, f32, vp, vp, vp, vp, vp, vp]),
+        "ra_causal_share_forward": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, i32,
+                                                   i32, vp, vp, vp, f32, vp, vp, vp, vp,
+                                                   vp]),
+        "ra_causal_pairs": (i64, [i32, i32, i64, i32]),
         "ra_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "ra_last_hip_error": (ctypes.c_int, []),
     }
@@ -75,7 +82,8 @@ def load():
 
 def exported_symbols() -> list[str]:
     return ["ra_ring_block", "ra_ring_schedule", "ra_kv_head", "ra_state_init", "ra_step",
-            "ra_finalize", "ra_share_forward", "ra_strerror", "ra_last_hip_error"]
+            "ra_finalize", "ra_share_forward", "ra_causal_share_forward", "ra_causal_pairs",
+            "ra_strerror", "ra_last_hip_error"]
 
 
 # ------------------------------------------------------------------ helpers
@@ -216,3 +224,46 @@ def share_forward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int,
         _dev(V, "V"), float(scale), _dev(O, "O"), _dev(m_out, "m_out"), _dev(l_out, "l_out"),
         _dev(O_cast, "O_cast"), _dev(sched_trace, "sched_trace"), _stream(stream)),
         "ra_share_forward")
+
+
+def _layout_code(layout) -> int:
+    if isinstance(layout, str):
+        if layout not in LAYOUTS:
+            raise ValueError(f"unknown layout {layout!r}")
+        return LAYOUTS[layout]
+    return int(layout)
+
+
+def causal_share_forward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int,
+                         layout, Q_i, K, V, scale: float, O, m_out=None, l_out=None,
+                         O_cast=None, stream=None):
+    """Rank `rank`'s causal share in one launch (see ra_causal_share_forward in ra.h).
+    `layout` is "contiguous", "striped", "zigzag" or an ra_layout code; K and V hold the
+    sequence in member-major order."""
+    if N < 1 or L % N != 0:
+        raise ValueError("L must be a multiple of N >= 1")
+    l = L // N
+    dt = Q_i.dtype
+    _need_shape(Q_i, (B, H, l, d), "Q_i")
+    _need_shape(K, (B, H_kv, L, d), "K", dt)
+    _need_shape(V, (B, H_kv, L, d), "V", dt)
+    _need_shape(O, (B, H, l, d), "O", torch.float32)
+    if m_out is not None:
+        _need_shape(m_out, (B, H, l), "m_out", torch.float32)
+    if l_out is not None:
+        _need_shape(l_out, (B, H, l), "l_out", torch.float32)
+    if O_cast is not None:
+        _need_shape(O_cast, (B, H, l, d), "O_cast", dt)
+    _check(load().ra_causal_share_forward(
+        rank, N, L, H, H_kv, d, B, _dtype_code(Q_i), _layout_code(layout), _dev(Q_i, "Q_i"),
+        _dev(K, "K"), _dev(V, "V"), float(scale), _dev(O, "O"), _dev(m_out, "m_out"),
+        _dev(l_out, "l_out"), _dev(O_cast, "O_cast"), _stream(stream)),
+        "ra_causal_share_forward")
+
+
+def causal_pairs(rank: int, N: int, L: int, layout) -> int:
+    """(query, key) pairs of member `rank`'s causal share per (batch, head) (host only)."""
+    n = int(load().ra_causal_pairs(rank, N, L, _layout_code(layout)))
+    if n < 0:
+        raise RaError(-n, "ra_causal_pairs")
+    return n

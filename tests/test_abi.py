@@ -162,3 +162,44 @@ def test_bf16_heads_beyond_the_32_bit_buffer_range_are_unsupported():
     assert _share(N=8, L=1 << 23, d=128) == ra.RA_ENOTSUP
     assert _share(N=8, L=1 << 24, d=64) == ra.RA_ENOTSUP
     assert _step(_shape(l_kv=1 << 23, kv_head_stride=0)) == ra.RA_ENOTSUP
+
+
+# ------------------------------------------------------------------ causal share
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("N,L", [(1, 64), (4, 64), (8, 8 * 256), (64, 64 * 128)])
+def test_causal_pairs_match_the_oracle_count(layout, N, L):
+    import oracle
+    for r in sorted({0, 1 % N, N // 2, N - 1}):
+        assert ra.causal_pairs(r, N, L, layout) == oracle.causal_pairs(r, N, L, layout)
+
+
+def test_causal_pairs_rejects_bad_arguments():
+    lib = ra.load()
+    for args in [(0, 0, 64, 0), (4, 4, 64, 0), (-1, 4, 64, 0), (0, 4, 65, 0), (0, 4, -4, 0),
+                 (0, 4, 64, 3), (0, 4, 64, -1), (0, 2, 6, ra.RA_LAYOUT_ZIGZAG)]:
+        assert lib.ra_causal_pairs(*args) == -ra.RA_EINVAL
+
+
+def _causal(**kw):
+    args = dict(rank=3, N=8, L=8 * 128, H=4, H_kv=2, d=128, B=1, dtype=ra.RA_BF16, layout=0,
+                Q=P, K=P, V=P, scale=0.088, O=P2, m=None, l=None, cast=None, stream=None)
+    args.update(kw)
+    return ra.load().ra_causal_share_forward(
+        args["rank"], args["N"], args["L"], args["H"], args["H_kv"], args["d"], args["B"],
+        args["dtype"], args["layout"], args["Q"], args["K"], args["V"], args["scale"],
+        args["O"], args["m"], args["l"], args["cast"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(layout=3), dict(layout=-1), dict(layout=2, L=8 * 64), dict(layout=2, L=8 * 192),
+    dict(N=0), dict(rank=8), dict(L=8 * 128 + 1), dict(H=5), dict(d=96), dict(dtype=9),
+    dict(scale=0.0), dict(Q=None), dict(O=MIS), dict(m=MIS), dict(cast=MIS),
+])
+def test_causal_share_rejects(kw):
+    assert _causal(**kw) == ra.RA_EINVAL
+
+
+def test_causal_share_limits_and_noop():
+    assert _causal(L=0, Q=None, K=None, V=None, O=None) == ra.RA_OK
+    assert _causal(N=8, L=1 << 23, d=128) == ra.RA_ENOTSUP
