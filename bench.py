@@ -9,6 +9,7 @@ are seeded synthetic tensors already resident in GPU memory.  Prints one JSON li
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -53,6 +54,11 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--step-path", action="store_true",
                    help="also time the per-step path (N x ra_step + ra_finalize)")
+    p.add_argument("--causal", choices=["contiguous", "striped", "zigzag"], default=None,
+                   help="time the causal share under this token layout instead")
+    p.add_argument("--rank", type=int, default=None, help="ring member to time")
+    p.add_argument("--causal-sweep", action="store_true",
+                   help="time every member's causal share under each layout (balance data)")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -88,6 +94,13 @@ def main():
     w = synth.WORKLOADS[name]
     if w.dtype != "bf16" or w.full_q:
         raise SystemExit("bench workloads are the bf16 single-share configurations")
+    if args.rank is not None:
+        if not 0 <= args.rank < w.N:
+            raise SystemExit(f"--rank must be in [0, {w.N})")
+        w = dataclasses.replace(w, rank=args.rank)
+    if args.causal_sweep:
+        causal_sweep(w, args)
+        return
     dev = torch.device("cuda:0")
     ra.load()
     print(f"[bench] drawing {name}", file=sys.stderr, flush=True)
@@ -97,7 +110,11 @@ def main():
     O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
 
     def step():
-        ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, scale, O)
+        if args.causal:
+            ra.causal_share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, args.causal, qd,
+                                    kd, vd, scale, O)
+        else:
+            ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, scale, O)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -115,10 +132,12 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
     print(f"[bench] {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
     flops = w.flops()
+    if args.causal:  # useful work only: the admissible (query, key) pairs
+        flops = 4.0 * w.d * w.B * w.H * ra.causal_pairs(w.rank, w.N, w.L, args.causal)
     tflops = flops / (ms * 1e-3) / 1e12
 
     extra = {}
-    if args.step_path:
+    if args.step_path and not args.causal:
         O_acc = torch.empty_like(O)
         m = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
         s = torch.empty_like(m)
@@ -142,7 +161,7 @@ def main():
         extra["step_path"] = {"ms": round(sp_ms, 4),
                               "tflops": round(flops / (sp_ms * 1e-3) / 1e12, 2)}
 
-    traffic = traffic_per_launch(name)
+    traffic = None if args.causal else traffic_per_launch(name)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
@@ -153,10 +172,21 @@ def main():
         import oracle
         Q, K, V = (synth.to_oracle_array(x) for x in (q, k, v))
         threads = oracle.max_threads()
+        if args.causal:
+            qpos = oracle.token_positions(args.causal, w.rank, w.N, w.l)
+            row_flops = lambda rows: float(np.sum(4.0 * w.d * (qpos[np.asarray(rows) % w.l] + 1)))
+
+            def run_oracle(rows):
+                return oracle.causal_share(Q, K, V, scale, w.rank, w.N, args.causal, rows=rows)
+        else:
+            row_flops = lambda rows: 4.0 * w.L * w.d * len(rows)
+
+            def run_oracle(rows):
+                return oracle.share(Q, K, V, scale, w.rank, w.N, rows=rows)
         per_row = 4.0 * w.L * w.d
         probe_rows = synth.sample_rows(w.B, w.H, w.l, 1, w.seed)[: max(8, threads)]
         t = time.perf_counter()
-        oracle.share(Q, K, V, scale, w.rank, w.N, rows=probe_rows)
+        run_oracle(probe_rows)
         probe_s = time.perf_counter() - t
         n_rows = int(max(len(probe_rows), len(probe_rows) * args.cpu_seconds / max(probe_s, 1e-3)))
         n_rows = min(n_rows, w.B * w.H * w.l)
@@ -165,20 +195,23 @@ def main():
         print(f"[bench] oracle baseline on {len(rows)} rows, {threads} threads",
               file=sys.stderr, flush=True)
         t = time.perf_counter()
-        ref, _, _ = oracle.share(Q, K, V, scale, w.rank, w.N, rows=rows)
+        ref, _, _ = run_oracle(rows)
         cpu_s = time.perf_counter() - t
-        cpu_tflops = len(rows) * per_row / cpu_s / 1e12
+        cpu_tflops = row_flops(rows) / cpu_s / 1e12
         cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": threads,
                         "kind": "oracle",
                         "sample": f"{len(rows)} random query rows of the same share "
-                                  f"({len(rows) * per_row:.3e} FLOP, {cpu_s:.1f} s, fp64)"}
+                                  f"({row_flops(rows):.3e} FLOP, {cpu_s:.1f} s, fp64)"}
         got = O.reshape(-1, w.d)[torch.tensor(rows, device=dev)].double().cpu().numpy()
         err = np.abs(got - ref)
         parity = {"rows": len(rows), "max_abs_err": float(err.max()),
                   "ok": bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))}
 
+    metric = "ring-share attention TFLOP/s (bf16) + % of MFMA peak at L=128K, N=8"
+    if args.causal:
+        metric = f"causal ring-share attention TFLOP/s, useful pairs only ({args.causal} layout)"
     line = {
-        "metric": "ring-share attention TFLOP/s (bf16) + % of MFMA peak at L=128K, N=8",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -191,7 +224,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded normal Q/K/V, resident in HBM)",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d, "L": w.L,
-                   "N": w.N, "rank": w.rank, "l": w.l, "flops_per_step": flops},
+                   "N": w.N, "rank": w.rank, "l": w.l, "flops_per_step": flops,
+                   **({"causal": args.causal} if args.causal else {})},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
@@ -200,6 +234,47 @@ def main():
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
+
+
+def causal_sweep(w, args):
+    """Every member's causal share under each layout: time per member and the spread
+    (the load-balance question of the slowleelab page, 4.5 limitation 2 and 4.8)."""
+    import torch
+
+    from long_context_exact_ra_amd import ra, synth
+    dev = torch.device("cuda:0")
+    q, k, v = synth.draw_workload(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    scale = 1.0 / math.sqrt(w.d)
+    O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    steps = max(1, args.steps // 4)
+    out = {"workload": w.name, "steps_per_rank": steps, "layouts": {}}
+    for layout in ("contiguous", "striped", "zigzag"):
+        ms = []
+        for r in range(w.N):
+            def step():
+                ra.causal_share_forward(r, w.N, w.L, w.H, w.H_kv, w.d, w.B, layout, qd, kd, vd,
+                                        scale, O)
+            step()
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for _ in range(steps):
+                step()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(t0.elapsed_time(t1) / steps)
+            print(f"[sweep] {layout} rank {r}: {ms[-1]:.3f} ms", file=sys.stderr, flush=True)
+        pairs = [ra.causal_pairs(r, w.N, w.L, layout) for r in range(w.N)]
+        useful = [4.0 * w.d * w.B * w.H * p / (t * 1e-3) / 1e12 for p, t in zip(pairs, ms)]
+        out["layouts"][layout] = {
+            "ms_per_rank": [round(x, 3) for x in ms],
+            "max_over_min": round(max(ms) / min(ms), 3),
+            "ring_step_ms": round(max(ms), 3),  # a ring waits for its slowest member
+            "useful_tflops_per_rank": [round(x, 1) for x in useful]}
+    print(json.dumps({"causal_sweep": out}), flush=True)
 
 
 if __name__ == "__main__":
