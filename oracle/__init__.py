@@ -23,6 +23,12 @@ causal_share(...), token_positions(...), causal_pairs(...)
     striped (interleaved) assignment of Striped Attention (4.8), and the zigzag
     assignment of two mirrored chunks per member (named in 4.5; the exact chunk
     pairing is this package's reading, see token_positions).
+share_backward(...), share_backward_rows(...)
+    Gradients of a share's output with respect to the resident queries and to every
+    K/V row it read, from the plain definition (aliyun page, FlashAttention section:
+    the backward pass recomputes the scores from the stored output and softmax
+    statistics instead of storing the attention matrix; the gradient itself is that of
+    softmax(scale Q K^T) V).  fp64 numpy, every matrix materialised.
 online_step(...)
     One merge of a K/V block into the running state (O_acc, m, l), in the order of
     the per-step pseudocode on the slowleelab page (section 4.3), fp64 numpy, with
@@ -254,6 +260,100 @@ def causal_pairs(rank: int, N: int, L: int, layout: str) -> int:
     q = token_positions(layout, rank, N, l)
     # positions 0..L-1 are each held once, so the keys at or before p number p + 1
     return int(np.sum(q + 1))
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of float32 arrays or bf16 bit patterns (uint16) to float64."""
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    raise TypeError("inputs must be float32 arrays or uint16 arrays holding bf16 bits")
+
+
+def _head_backward(q, k, v, do, scale, mask=None):
+    """One (query head, kv head) pair: q, do [n, d]; k, v [m, d] fp64; mask [n, m] bool
+    (True = admissible) or None.  The softmax of each query row is over its admissible
+    keys; the gradient of O = P V is taken through P = softmax(S), S = scale q k^T:
+        dV = P^T dO,  dP = dO V^T,
+        dS = P * (dP - sum_k P dP)      (the softmax Jacobian, row by row)
+        dQ = scale dS K,  dK = scale dS^T Q."""
+    S = scale * (q @ k.T)
+    if mask is not None:
+        S = np.where(mask, S, -np.inf)
+    M = S.max(axis=1, keepdims=True)
+    P = np.exp(S - M)
+    P /= P.sum(axis=1, keepdims=True)
+    dV = P.T @ do
+    dP = do @ v.T
+    dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+    return scale * (dS @ k), scale * (dS.T @ q), dV
+
+
+def share_backward(Q, K, V, dO, scale, rank: int = 0, N: int = 1, layout: str | None = None):
+    """Gradients of member `rank`'s share output O_i = softmax(scale Q_i K^T) V over all L
+    keys (or, with `layout`, over its admissible keys as in causal_share), given the
+    upstream gradient dO_i.  Returns (dQ_i [B, H, l, d], dK [B, H_kv, L, d],
+    dV [B, H_kv, L, d]) in fp64: dK and dV hold this member's contribution to every key
+    row; with grouped K/V heads the contributions of a group's query heads add up.
+    The ring order does not enter: the share is a softmax over a set of keys."""
+    q, k, v, do = (_f64(x) for x in (Q, K, V, dO))
+    B, H, l, d = q.shape
+    H_kv, L = k.shape[1], k.shape[2]
+    g = H // H_kv
+    mask = None
+    if layout is not None:
+        mask = (layout_positions(layout, N, L)[None, :]
+                <= token_positions(layout, rank, N, l)[:, None])
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            a, bk, c = _head_backward(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, mask)
+            dQ[b, h] = a
+            dK[b, h // g] += bk
+            dV[b, h // g] += c
+    return dQ, dK, dV
+
+
+def share_backward_rows(Q, K, V, dO, scale, heads, q_rows, k_rows, chunk: int = 512):
+    """Sampled gradients for large shares, without materialising l x L per head at once.
+    heads: list of (b, h) query heads; q_rows / k_rows: local query rows and key rows to
+    report for each of them.  Returns, per head, (dQ[q_rows] [nq, d], dK_part[k_rows],
+    dV_part[k_rows]) where the K/V parts are this query head's contribution only.
+    Same formulas as share_backward, evaluated in query chunks: the softmax statistics
+    of every query row are computed first (they are what the backward pass reuses)."""
+    q_all, k_all, v_all, do_all = Q, K, V, dO
+    H = q_all.shape[1]
+    H_kv = k_all.shape[1]
+    g = H // H_kv
+    out = []
+    for (b, h) in heads:
+        q = _f64(q_all[b, h])
+        k = _f64(k_all[b, h // g])
+        v = _f64(v_all[b, h // g])
+        do = _f64(do_all[b, h])
+        l = q.shape[0]
+        kr = np.asarray(k_rows, dtype=np.int64)
+        dK = np.zeros((kr.size, q.shape[1]))
+        dV = np.zeros_like(dK)
+        dQ = np.zeros((len(q_rows), q.shape[1]))
+        qset = {int(r): i for i, r in enumerate(q_rows)}
+        for c0 in range(0, l, chunk):
+            c1 = min(l, c0 + chunk)
+            S = scale * (q[c0:c1] @ k.T)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dP = do[c0:c1] @ v.T
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dV += P[:, kr].T @ do[c0:c1]
+            dK += scale * (dS[:, kr].T @ q[c0:c1])
+            for r in range(c0, c1):
+                if r in qset:
+                    dQ[qset[r]] = scale * (dS[r - c0] @ k)
+        out.append((dQ, dK, dV))
+    return out
 
 
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
