@@ -195,6 +195,36 @@ int ra_causal_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32
  */
 int64_t ra_causal_pairs(int32_t rank, int32_t N, int64_t L, int32_t layout);
 
+/*
+ * Gradients of ring member `rank`'s (non-causal) share, bf16 inputs
+ * (aliyun FlashAttention explainer, section 2: the backward pass recomputes the scores
+ * from the stored output O and the softmax statistics instead of storing the attention
+ * matrix).  With lse = m + ln(l) from ra_share_forward and D_r = dO_r . O_r:
+ *     P  = exp(scale Q_i K^T - lse),   dS = P * (dO_i V^T - D)
+ *     dQ_i = scale dS K,   dK += scale dS^T Q_i,   dV += P^T dO_i
+ * over all L keys of the sequence (a share's softmax runs over every block, so the ring
+ * order does not enter the gradient).
+ *   Q_i, K, V  as in ra_share_forward (dtype must be RA_BF16, else RA_ENOTSUP)
+ *   O          fp32 [B, H, l, d]: the forward output of the same share
+ *   dO         [B, H, l, d] in `dtype`: the gradient of the loss with respect to O
+ *   m, l       fp32 [B, H, l]: the forward's m_out and l_out
+ *   dQ         fp32 [B, H, l, d], written
+ *   dK, dV     fp32 [B, H_kv, L, d], ADDED to (zero them first; a ring passes them
+ *              along with their K/V block and every member adds its part)
+ *   workspace  device buffer of ra_share_backward_workspace(B, H, L / N) bytes, 16-byte
+ *              aligned, owned by the caller; its contents are scratch
+ * L == 0 is a no-op.  Other arguments and errors as in ra_share_forward.
+ */
+int ra_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, int32_t d,
+                      int32_t B, int32_t dtype, const void *Q_i, const void *K, const void *V,
+                      const float *O, const void *dO, const float *m, const float *l,
+                      float scale, float *dQ, float *dK, float *dV, void *workspace,
+                      void *stream);
+
+/* Bytes of workspace ra_share_backward needs for B x H query rows of length l_q:
+ * 8 * B * H * l_q (two floats per row).  Returns -RA_EINVAL for negative sizes. */
+int64_t ra_share_backward_workspace(int32_t B, int32_t H, int64_t l_q);
+
 /* Static description of a status code. */
 const char *ra_strerror(int status);
 

@@ -264,6 +264,60 @@ int64_t ra_causal_pairs(int32_t rank, int32_t N, int64_t L, int32_t layout) {
     }
 }
 
+int64_t ra_share_backward_workspace(int32_t B, int32_t H, int64_t l_q) {
+    if (B < 0 || H < 0 || l_q < 0) return -RA_EINVAL;
+    return 8 * (int64_t)B * H * l_q;
+}
+
+int ra_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, int32_t d,
+                      int32_t B, int32_t dtype, const void *Q_i, const void *K, const void *V,
+                      const float *O, const void *dO, const float *m, const float *l,
+                      float scale, float *dQ, float *dK, float *dV, void *workspace,
+                      void *stream) {
+    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
+        !heads_ok(B, H, H_kv, d, dtype) || !scale_ok(scale))
+        return RA_EINVAL;
+    if (L == 0) return RA_OK;
+    if (!ptr_ok(Q_i) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(O) || !ptr_ok(dO) || !ptr_ok(m) ||
+        !ptr_ok(l) || !ptr_ok(dQ) || !ptr_ok(dK) || !ptr_ok(dV) || !ptr_ok(workspace))
+        return RA_EINVAL;
+    if (dtype != RA_BF16) return RA_ENOTSUP;  // the backward kernels take bf16 inputs
+    const int64_t lq = L / N;
+    if (!head_range_ok(dtype, L, d) || !head_range_ok(dtype, lq, d) ||
+        lq > (int64_t)INT32_MAX / 8)  // one head's statistics through a 32-bit buffer range
+        return RA_ENOTSUP;
+    ra::BwdArgs a{};
+    const int64_t qt = (lq + ra::bwd_query_tile() - 1) / ra::bwd_query_tile();
+    const int64_t kt = (L + ra::bwd_key_tile() - 1) / ra::bwd_key_tile();
+    if (qt * B * H > INT32_MAX || kt * B * H_kv > INT32_MAX) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    a.Q = Q_i;
+    a.K = K;
+    a.V = V;
+    a.dO = dO;
+    a.ws = (float *)workspace;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.l_q = lq;
+    a.L = L;
+    a.kv_head_stride = L * d;
+    a.kv_batch_stride = (int64_t)H_kv * L * d;
+    a.H = H;
+    a.H_kv = H_kv;
+    a.group = H / H_kv;
+    a.n_qtiles = (int32_t)qt;
+    a.n_wg = (int32_t)(qt * B * H);
+    a.n_ktiles = (int32_t)kt;
+    a.n_kv_wg = (int32_t)(kt * B * H_kv);
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipStream_t st = (hipStream_t)stream;
+    return after_launch(
+        ra::launch_bwd_bf16(a, O, dO, m, l, (int64_t)B * H * lq, d, st), st);
+}
+
 const char *ra_strerror(int status) {
     switch (status) {
     case RA_OK: return "success";

@@ -41,6 +41,31 @@ struct FwdArgs {
 
 constexpr int32_t kNoCausal = -1;
 
+// Work description of the backward kernels (one share's gradients).
+struct BwdArgs {
+    const void *Q;    // [B, H, l_q, D] contiguous
+    const void *K;    // head (b, g) at K + b*kv_batch_stride + g*kv_head_stride, L rows
+    const void *V;
+    const void *dO;   // [B, H, l_q, D] contiguous, same dtype as Q
+    float *ws;        // [B, H, l_q] pairs (D = dO . O, lse * log2(e)), written by prep
+    float *dQ;        // [B, H, l_q, D] written
+    float *dK;        // [B, H_kv, L, D] (kv strides) added to
+    float *dV;
+    int64_t l_q;
+    int64_t L;
+    int64_t kv_head_stride;
+    int64_t kv_batch_stride;
+    int32_t H;
+    int32_t H_kv;
+    int32_t group;      // H / H_kv
+    int32_t n_qtiles;   // dQ: query tiles per (batch, head)
+    int32_t n_wg;       // dQ work-groups
+    int32_t n_ktiles;   // dK/dV: key tiles per (batch, kv head)
+    int32_t n_kv_wg;    // dK/dV work-groups
+    float scale;
+    float scale_log2;
+};
+
 enum Mode : int {
     MODE_SHARE = 0,  // no state in; finalised output out
     MODE_STEP = 1    // running state in and out, no division
@@ -51,6 +76,11 @@ int bf16_query_tile();
 constexpr int kF32QueryTile = 64;
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int B, int d, int mode, hipStream_t st);
+// Rows per work-group of the backward kernels (query rows for dQ, key rows for dK/dV).
+int bwd_query_tile();
+int bwd_key_tile();
+hipError_t launch_bwd_bf16(const BwdArgs &a, const float *O, const void *dO, const float *m,
+                           const float *l, int64_t rows, int d, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs &a, int B, int d, int mode, hipStream_t st);
 hipError_t launch_state_init(float *O_acc, float *m, float *l, int64_t rows, int d,
                              hipStream_t st);
