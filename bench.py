@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--causal", choices=["contiguous", "striped", "zigzag"], default=None,
                    help="time the causal share under this token layout instead")
     p.add_argument("--rank", type=int, default=None, help="ring member to time")
+    p.add_argument("--backward", action="store_true",
+                   help="time the share's backward pass (ra_share_backward) instead")
     p.add_argument("--causal-sweep", action="store_true",
                    help="time every member's causal share under each layout (balance data)")
     p.add_argument("--copy-calib", action="store_true",
@@ -109,8 +111,26 @@ def main():
     scale = 1.0 / math.sqrt(w.d)
     O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
 
-    def step():
+    if args.backward:
         if args.causal:
+            raise SystemExit("the backward pass covers the non-causal share")
+        g = torch.Generator().manual_seed(w.seed + 99)
+        dOd = torch.randn((w.B, w.H, w.l, w.d), generator=g).to(torch.bfloat16).to(dev)
+        m_f = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
+        l_f = torch.empty_like(m_f)
+        ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, scale, O, m_f,
+                         l_f)
+        dQ = torch.empty_like(O)
+        dK = torch.zeros((w.B, w.H_kv, w.L, w.d), dtype=torch.float32, device=dev)
+        dV = torch.zeros_like(dK)
+        ws = torch.empty((max(16, int(ra.load().ra_share_backward_workspace(w.B, w.H, w.l))),),
+                         dtype=torch.uint8, device=dev)
+
+    def step():
+        if args.backward:
+            ra.share_backward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, O, dOd,
+                              m_f, l_f, scale, dQ, dK, dV, ws)
+        elif args.causal:
             ra.causal_share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, args.causal, qd,
                                     kd, vd, scale, O)
         else:
@@ -132,12 +152,14 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
     print(f"[bench] {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
     flops = w.flops()
+    if args.backward:  # S, dP, dV, dK, dQ products: 2.5x the forward's two
+        flops = 2.5 * w.flops()
     if args.causal:  # useful work only: the admissible (query, key) pairs
         flops = 4.0 * w.d * w.B * w.H * ra.causal_pairs(w.rank, w.N, w.L, args.causal)
     tflops = flops / (ms * 1e-3) / 1e12
 
     extra = {}
-    if args.step_path and not args.causal:
+    if args.step_path and not args.causal and not args.backward:
         O_acc = torch.empty_like(O)
         m = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
         s = torch.empty_like(m)
@@ -161,14 +183,16 @@ def main():
         extra["step_path"] = {"ms": round(sp_ms, 4),
                               "tflops": round(flops / (sp_ms * 1e-3) / 1e12, 2)}
 
-    traffic = None if args.causal else traffic_per_launch(name)
+    traffic = None if (args.causal or args.backward) else traffic_per_launch(name)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
 
     cpu_baseline = None
     parity = None
-    if not args.no_cpu_baseline:
+    if args.backward and not args.no_cpu_baseline:
+        cpu_baseline, parity = backward_cpu_baseline(w, q, k, v, dOd, dQ, scale, args)
+    elif not args.no_cpu_baseline:
         import oracle
         Q, K, V = (synth.to_oracle_array(x) for x in (q, k, v))
         threads = oracle.max_threads()
@@ -210,6 +234,8 @@ def main():
     metric = "ring-share attention TFLOP/s (bf16) + % of MFMA peak at L=128K, N=8"
     if args.causal:
         metric = f"causal ring-share attention TFLOP/s, useful pairs only ({args.causal} layout)"
+    if args.backward:
+        metric = "ring-share attention backward TFLOP/s (bf16; 2.5x forward FLOPs)"
     line = {
         "metric": metric,
         "value": round(tflops, 2),
@@ -225,7 +251,8 @@ def main():
         "data": "synthetic (seeded normal Q/K/V, resident in HBM)",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d, "L": w.L,
                    "N": w.N, "rank": w.rank, "l": w.l, "flops_per_step": flops,
-                   **({"causal": args.causal} if args.causal else {})},
+                   **({"causal": args.causal} if args.causal else {}),
+                   **({"pass": "backward"} if args.backward else {})},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
@@ -234,6 +261,33 @@ def main():
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
+
+
+def backward_cpu_baseline(w, q, k, v, dOd, dQ, scale, args):
+    """The oracle's dQ rows of the same backward on a bounded sample of query rows of one
+    head (each needs that head's full softmax statistics, computed in query chunks)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from long_context_exact_ra_amd import synth
+    Q, K, V, dO = (synth.to_oracle_array(x) for x in (q, k, v, dOd.cpu()))
+    h = w.H // 2
+    t = time.perf_counter()
+    n = 8
+    res = oracle.share_backward_rows(Q, K, V, dO, scale, [(0, h)], list(range(n)), [])
+    probe = time.perf_counter() - t
+    # one head's statistics dominate: l x L x d x 4 FLOP, plus the sampled rows
+    stat_flops = 4.0 * w.l * w.L * w.d
+    cpu_tflops = stat_flops / probe / 1e12
+    got = dQ[0, h, :n].double().cpu().numpy()
+    ref = res[0][0]
+    err = float(np.abs(got - ref).max())
+    return ({"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+             "kind": "oracle",
+             "sample": f"one head's backward statistics and {n} dQ rows "
+                       f"({stat_flops:.3e} FLOP, {probe:.1f} s, fp64 numpy)"},
+            {"rows": n, "max_abs_err": err, "ok": bool(err <= 2e-2 * np.abs(ref).max() + 1e-5)})
 
 
 def causal_sweep(w, args):
