@@ -291,9 +291,11 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int NKK = D / 16, NDT = D / 32, TILE = QBC * D;
     using TL = TileLoad<D, QBC, KW>;
-    __shared__ __attribute__((aligned(1024))) bf16 Qt[2][TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 Ot[2][TILE];  // dO tiles
-    __shared__ __attribute__((aligned(16))) f32x2 Wt[2][QBC];    // (D, lse2) of the rows
+    // Three tile buffers: tile t is read by the gradient products while tile t+1 is read
+    // by the score products and tile t+2 is being loaded.
+    __shared__ __attribute__((aligned(1024))) bf16 Qt[3][TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Ot[3][TILE];  // dO tiles
+    __shared__ __attribute__((aligned(16))) f32x2 Wt[3][QBC];    // (D, lse2) of the rows
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -356,24 +358,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int tb_lo = tr_base<D>(lane, 0), tb_hi = tr_base<D>(lane, 1);
     const float c = a.scale_log2;
 
-    load(0, 0);
-    for (int32_t t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (t + 1 < n_tiles) load(t + 1, buf ^ 1);
+    // S = Q K^T and dP = dO V^T of the tile in buffer `buf`: lane = key ln, 16 queries per
+    // 32-query block, element i of block qb = query 32 qb + 8 (i/4) + 4 hf + i%4.
+    auto scores = [&](int buf, f32x16 *sc, f32x16 *dq) {
         const bf16 *qt = Qt[buf], *ot = Ot[buf];
-        const int32_t s_idx = t % tiles_per_head;
-        const int64_t left = a.l_q - (int64_t)s_idx * QBC;
-        const int qlim = (left < QBC ? (int)left : QBC) - 4 * hf;  // valid query rows
-
-        // S = Q K^T and dP = dO V^T: lane = key ln, 16 queries per 32-query block,
-        // element i of block qb = query 32 qb + 8 (i/4) + 4 hf + i%4.
-        f32x16 s[2], dp[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = f32x16{};
-            dp[qb] = f32x16{};
+            sc[qb] = f32x16{};
+            dq[qb] = f32x16{};
         }
         int kb = rb;
         asm volatile("" : "+v"(kb));
@@ -384,15 +376,20 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 const int off = (kb ^ (16 * kk)) + 32 * qb * D;
                 const bf16x8 qa = *(const bf16x8 *)(qt + off);
                 const bf16x8 oa = *(const bf16x8 *)(ot + off);
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s[qb], 0, 0, 0);
-                dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp[qb], 0, 0, 0);
+                sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sc[qb], 0, 0, 0);
+                dq[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dq[qb], 0, 0, 0);
             }
         }
-        // P and dS per element; rows past the end of the block get P = 0.  Packed in the
-        // contraction order of the gradient products (operand c4: queries
-        // 16 c4 + 8 (j/4) + 4 hf + j%4 = elements 8 (c4%2) + j of block c4/2).
+    };
+    // P and dS of tile t; rows past the end of the block get P = 0.  Packed in the
+    // contraction order of the gradient products (operand c4: queries
+    // 16 c4 + 8 (j/4) + 4 hf + j%4 = elements 8 (c4%2) + j of block c4/2).
+    auto softmax = [&](int buf, int32_t t, const f32x16 *sc, const f32x16 *dq, bf16x8 *pp,
+                       bf16x8 *dsp) {
+        const int32_t s_idx = t % tiles_per_head;
+        const int64_t left = a.l_q - (int64_t)s_idx * QBC;
+        const int qlim = (left < QBC ? (int)left : QBC) - 4 * hf;  // valid query rows
         const f32x2 *w = Wt[buf];
-        bf16x8 pp[4], dsp[4];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
@@ -406,13 +403,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * j4 + e, i = 8 * (c4 & 1) + j;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c4 >> 1][i], c, -Lq[e]));
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c4 >> 1][i], c, -Lq[e]));
                     if (q0 + e >= qlim) p = 0.f;
                     pp[c4][j] = (bf16)p;
-                    dsp[c4][j] = (bf16)(p * (dp[c4 >> 1][i] - Dq[e]));
+                    dsp[c4][j] = (bf16)(p * (dq[c4 >> 1][i] - Dq[e]));
                 }
             }
-        // dV^T += dO^T P and dK^T += Q^T dS: A = transposed reads of the dO / Q tiles.
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS: A = transposed reads of the dO / Q tiles.
+    auto grads = [&](int buf, const bf16x8 *pp, const bf16x8 *dsp) {
+        const bf16 *qt = Qt[buf], *ot = Ot[buf];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
@@ -426,6 +426,28 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pp[c4], dv[dt], 0, 0, 0);
                 dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsp[c4], dk[dt], 0, 0, 0);
             }
+    };
+
+    // Pipeline: iteration t runs the exponentials of tile t beside the score products of
+    // tile t+1, then tile t's gradient products; tile t+2 loads meanwhile.
+    load(0, 0);
+    if (n_tiles > 1) load(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    f32x16 s[2], dp[2];
+    scores(0, s, dp);
+    int buf = 0;  // buffer of tile t
+    for (int32_t t = 0; t < n_tiles; ++t) {
+        const int nb = buf == 2 ? 0 : buf + 1;    // tile t + 1
+        const int nnb = nb == 2 ? 0 : nb + 1;     // tile t + 2 (held tile t - 1)
+        if (t + 2 < n_tiles) load(t + 2, nnb);
+        bf16x8 pp[4], dsp[4];
+        softmax(buf, t, s, dp, pp, dsp);
+        if (t + 1 < n_tiles) scores(nb, s, dp);
+        grads(buf, pp, dsp);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // tile t + 2 landed (this wave's part)
+        __syncthreads();                     // everyone's part; tile t fully read
+        buf = nb;
     }
 
     if (!kvalid) return;
