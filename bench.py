@@ -112,14 +112,16 @@ def main():
     O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
 
     if args.backward:
-        if args.causal:
-            raise SystemExit("the backward pass covers the non-causal share")
         g = torch.Generator().manual_seed(w.seed + 99)
         dOd = torch.randn((w.B, w.H, w.l, w.d), generator=g).to(torch.bfloat16).to(dev)
         m_f = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
         l_f = torch.empty_like(m_f)
-        ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, scale, O, m_f,
-                         l_f)
+        if args.causal:
+            ra.causal_share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, args.causal, qd,
+                                    kd, vd, scale, O, m_f, l_f)
+        else:
+            ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, scale, O,
+                             m_f, l_f)
         dQ = torch.empty_like(O)
         dK = torch.zeros((w.B, w.H_kv, w.L, w.d), dtype=torch.float32, device=dev)
         dV = torch.zeros_like(dK)
@@ -127,7 +129,10 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     def step():
-        if args.backward:
+        if args.backward and args.causal:
+            ra.causal_share_backward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, args.causal, qd,
+                                     kd, vd, O, dOd, m_f, l_f, scale, dQ, dK, dV, ws)
+        elif args.backward:
             ra.share_backward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, qd, kd, vd, O, dOd,
                               m_f, l_f, scale, dQ, dK, dV, ws)
         elif args.causal:
@@ -156,6 +161,8 @@ def main():
         flops = 2.5 * w.flops()
     if args.causal:  # useful work only: the admissible (query, key) pairs
         flops = 4.0 * w.d * w.B * w.H * ra.causal_pairs(w.rank, w.N, w.L, args.causal)
+        if args.backward:
+            flops *= 2.5
     tflops = flops / (ms * 1e-3) / 1e12
 
     extra = {}
@@ -236,6 +243,9 @@ def main():
         metric = f"causal ring-share attention TFLOP/s, useful pairs only ({args.causal} layout)"
     if args.backward:
         metric = "ring-share attention backward TFLOP/s (bf16; 2.5x forward FLOPs)"
+        if args.causal:
+            metric = ("causal ring-share attention backward TFLOP/s, useful pairs only "
+                      f"({args.causal} layout; 2.5x forward FLOPs)")
     line = {
         "metric": metric,
         "value": round(tflops, 2),
@@ -275,10 +285,14 @@ def backward_cpu_baseline(w, q, k, v, dOd, dQ, scale, args):
     h = w.H // 2
     t = time.perf_counter()
     n = 8
-    res = oracle.share_backward_rows(Q, K, V, dO, scale, [(0, h)], list(range(n)), [])
+    res = oracle.share_backward_rows(Q, K, V, dO, scale, [(0, h)], list(range(n)), [],
+                                     rank=w.rank, N=w.N, layout=args.causal)
     probe = time.perf_counter() - t
-    # one head's statistics dominate: l x L x d x 4 FLOP, plus the sampled rows
-    stat_flops = 4.0 * w.l * w.L * w.d
+    # one head's statistics dominate: 4 d FLOP per (query, key) pair (the admissible
+    # pairs only, for a causal share), plus the sampled rows
+    pairs = (w.l * w.L if not args.causal else
+             oracle.causal_pairs(w.rank, w.N, w.L, args.causal))
+    stat_flops = 4.0 * pairs * w.d
     cpu_tflops = stat_flops / probe / 1e12
     got = dQ[0, h, :n].double().cpu().numpy()
     ref = res[0][0]

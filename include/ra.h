@@ -221,7 +221,25 @@ int ra_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_k
                       float scale, float *dQ, float *dK, float *dV, void *workspace,
                       void *stream);
 
-/* Bytes of workspace ra_share_backward needs for B x H query rows of length l_q:
+/*
+ * Gradients of ring member `rank`'s causal share (the share of ra_causal_share_forward:
+ * each query's softmax runs over the keys at or before its position, slowleelab "Ring
+ * Attention" page, 4.5 limitation 2; positions from `layout` as there).  Same formulas
+ * as ra_share_backward with P = 0 on the excluded pairs; key rows no query of the share
+ * sees get nothing added.  The kernels skip the key tiles (for dQ) and query tiles (for
+ * dK, dV) that hold no admissible pair.
+ *   layout   an ra_layout; RA_LAYOUT_ZIGZAG needs l to be a multiple of 128, else
+ *            RA_EINVAL
+ *   O, m, l  the outputs of ra_causal_share_forward for the same share and layout
+ * Other arguments, ownership and errors as in ra_share_backward.
+ */
+int ra_causal_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                             int32_t d, int32_t B, int32_t dtype, int32_t layout,
+                             const void *Q_i, const void *K, const void *V, const float *O,
+                             const void *dO, const float *m, const float *l, float scale,
+                             float *dQ, float *dK, float *dV, void *workspace, void *stream);
+
+/* Bytes of workspace ra_share_backward (and ra_causal_share_backward) needs for B x H query rows of length l_q:
  * 8 * B * H * l_q (two floats per row).  Returns -RA_EINVAL for negative sizes. */
 int64_t ra_share_backward_workspace(int32_t B, int32_t H, int64_t l_q);
 

@@ -27,6 +27,17 @@
 //    elementwise P / dS work is in-lane, and the bf16-packed P and dS are directly the B
 //    operands of the gradient products (the key / query order inside each 16-deep
 //    contraction is permuted to match, as in the forward kernel).
+//
+// Causal shares (one K/V block per ring member, token positions from the layout): the
+// dQ kernel walks only the key tiles of each block that some query of its tile may
+// attend to (a prefix of the block) and limits each lane's keys on the partial ones;
+// the dK/dV kernel walks only the query tiles from the first one holding a query at
+// or after its first key (a suffix) and masks each (query, key) pair by a per-lane
+// threshold (one compare more per element than the ragged-tail mask).  Work-groups
+// with the most work are dispatched first.
+#include <type_traits>
+
+#include "causal_map.h"
 #include "ra_internal.h"
 
 namespace ra {
@@ -147,7 +158,7 @@ constexpr int QW = 8;         // waves per dQ work-group, 32 query rows each
 constexpr int QBR = 32 * QW;  // query rows per dQ work-group
 constexpr int KBC = 64;       // keys per streamed K/V tile
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NKK = D / 16, NDT = D / 32, TILE = KBC * D;
     using TL = TileLoad<D, KBC, QW>;
@@ -158,7 +169,9 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5, ln = lane & 31;
     const int wg = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, a.n_wg));
-    const int qt = __builtin_amdgcn_readfirstlane(wg % a.n_qtiles);
+    // Causal: the last query tiles of a head see the most keys; they go first.
+    const int qt = __builtin_amdgcn_readfirstlane(
+        CAUSAL ? a.n_qtiles - 1 - wg % a.n_qtiles : wg % a.n_qtiles);
     const int bh = __builtin_amdgcn_readfirstlane(wg / a.n_qtiles);
     const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
     const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
@@ -198,26 +211,61 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void *)Kh, 0, head_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void *)Vh, 0, head_bytes, kRsrcWord3);
-    const int32_t n_tiles = (int32_t)((a.L + KBC - 1) / KBC);
-    auto load = [&](int32_t t, int buf) {
-        const int64_t r0 = (int64_t)t * KBC;
-        const int64_t left = a.L - r0;
-        const int valid = left < KBC ? (int)left : KBC;
+    // Key tiles: tile tin of block j holds keys j*kblk + tin*KBC ... (never two blocks).
+    const int32_t kblk = (int32_t)a.kblk_rows;  // host: a head's rows fit in int32
+    const int32_t tiles_per_blk = (kblk + KBC - 1) / KBC;
+    const CausalMap cmap{a.layout, a.rank, a.n_kblocks, kblk};
+    const int32_t a_end = (int32_t)(a.l_q < (int64_t)(qt + 1) * QBR ? a.l_q : (qt + 1) * QBR);
+    auto act_of = [&](int32_t j) -> int32_t {  // active tiles of block j (a prefix)
+        if constexpr (!CAUSAL) return tiles_per_blk;
+        else return cmap.active_tiles(j, a_end - 1, KBC, tiles_per_blk);
+    };
+    int32_t n_tiles = tiles_per_blk * a.n_kblocks;
+    if constexpr (CAUSAL) {
+        n_tiles = 0;
+        for (int32_t j = 0; j < a.n_kblocks; ++j) n_tiles += act_of(j);
+    }
+    struct Cursor {
+        int32_t j, tin, act;
+    };
+    auto advance = [&](Cursor &cu) {
+        if (++cu.tin < cu.act) return;
+        cu.tin = 0;
+        do {
+            ++cu.j;
+        } while (cu.j < a.n_kblocks && (cu.act = act_of(cu.j)) == 0);
+    };
+    auto tile_rows = [&](const Cursor &cu) {
+        const int32_t left = kblk - cu.tin * KBC;
+        return left < KBC ? left : KBC;
+    };
+    auto load = [&](const Cursor &cu, int buf) {
+        const int64_t r0 = (int64_t)cu.j * kblk + (int64_t)cu.tin * KBC;
         const uint32_t soff = (uint32_t)(r0 * D * 2);
-        TL::run(krs, soff, valid, Kt[buf], wave, lane);
-        TL::run(vrs, soff, valid, Vt[buf], wave, lane);
+        TL::run(krs, soff, tile_rows(cu), Kt[buf], wave, lane);
+        TL::run(vrs, soff, tile_rows(cu), Vt[buf], wave, lane);
     };
 
     const int rb = row_base<D>(ln, hf);
     const int tb_lo = tr_base<D>(lane, 0), tb_hi = tr_base<D>(lane, 1);
     const float c = a.scale_log2;
 
-    load(0, 0);
+    const int32_t qa = qt * QBR + qloc;  // this lane's local query
+    Cursor lc{-1, 0, 0}, cc;             // next tile to load; tile being computed
+    advance(lc);
+    cc = lc;
+    if (n_tiles > 0) {
+        load(lc, 0);
+        advance(lc);
+    }
     for (int32_t t = 0; t < n_tiles; ++t) {
         const int buf = t & 1;
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t landed (this wave's part)
         __syncthreads();                     // ... everyone's part; tile t-1 fully read
-        if (t + 1 < n_tiles) load(t + 1, buf ^ 1);
+        if (t + 1 < n_tiles) {
+            load(lc, buf ^ 1);
+            advance(lc);
+        }
         const bf16 *kt = Kt[buf], *vt = Vt[buf];
 
         // S^T = K Q^T and dP^T = V dO^T: lane = query ln, 16 keys per 32-key block.
@@ -240,11 +288,17 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
                 dp[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kk], dp[k2], 0, 0, 0);
             }
         }
-        // dS = P (dP - D), P = exp2(s c - lse2); keys past the end get P = 0.  Packed in
-        // the contraction order of the dQ product: operand c4 holds keys
-        // 16 c4 + 8 (j/4) + 4 hf + j%4, i.e. elements 8 (c4%2) + j of block c4/2.
-        const int64_t left = a.L - (int64_t)t * KBC;
-        const int lim = (left < KBC ? (int)left : KBC) - 4 * hf;
+        // dS = P (dP - D), P = exp2(s c - lse2); keys past the end of the block (and,
+        // causal, keys after this lane's query) get P = 0.  Packed in the contraction
+        // order of the dQ product: operand c4 holds keys 16 c4 + 8 (j/4) + 4 hf + j%4,
+        // i.e. elements 8 (c4%2) + j of block c4/2.
+        int keys = tile_rows(cc);
+        if constexpr (CAUSAL) {
+            const int allow = cmap.allowed(qa, cc.j, cc.tin * KBC);
+            keys = allow < keys ? (allow > 0 ? allow : 0) : keys;
+        }
+        const int lim = keys - 4 * hf;
+        advance(cc);
         bf16x8 dsp[4];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
@@ -286,7 +340,31 @@ constexpr int KW = 4;         // waves per dK/dV work-group (one per SIMD), 32 k
 constexpr int KBR = 32 * KW;  // key rows per work-group
 constexpr int QBC = 64;       // query rows per streamed Q / dO tile
 
-template <int D>
+// Causal: key tile i of a (batch, kv head) in order of its first key's position (the
+// earliest keys are seen by the most queries, so they go first).  Zigzag lists the first
+// halves of the blocks, then the second halves from the last block down.
+__device__ __forceinline__ void key_tile_of(int32_t i, int32_t layout, int32_t N, int32_t kpb,
+                                            int32_t &j, int32_t &u) {
+    if (layout == kLayoutContiguous) {
+        j = i / kpb;
+        u = i - j * kpb;
+    } else if (layout == kLayoutStriped) {
+        u = i / N;
+        j = i - u * N;
+    } else {
+        const int32_t ka = (kpb + 1) / 2, kb = kpb - ka;
+        if (i < N * ka) {
+            j = i / ka;
+            u = i - j * ka;
+        } else {
+            const int32_t r = i - N * ka, jj = r / kb;
+            j = N - 1 - jj;
+            u = ka + (r - jj * kb);
+        }
+    }
+}
+
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int NKK = D / 16, NDT = D / 32, TILE = QBC * D;
@@ -306,8 +384,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int g = __builtin_amdgcn_readfirstlane(bg % a.H_kv);
     const int b = __builtin_amdgcn_readfirstlane(bg / a.H_kv);
 
-    const int64_t key = (int64_t)kt_i * KBR + wave * 32 + ln;  // this lane's key row
-    const bool kvalid = key < a.L;
+    // Key tile kt_i is tile u of key block j; this lane's key is local key bl of block j.
+    int32_t j = 0, u = kt_i;
+    if constexpr (CAUSAL) key_tile_of(kt_i, a.layout, a.n_kblocks, a.n_ktiles_blk, j, u);
+    j = __builtin_amdgcn_readfirstlane(j);
+    u = __builtin_amdgcn_readfirstlane(u);
+    const int32_t kblk = (int32_t)a.kblk_rows;
+    const int32_t bl = u * KBR + wave * 32 + ln;
+    const int64_t key = (int64_t)j * kblk + bl;  // this lane's key row
+    const bool kvalid = bl < kblk;
     const int64_t kvoff = b * a.kv_batch_stride + g * a.kv_head_stride;
 
     // Resident B operands: K and V rows of this lane's key.
@@ -330,10 +415,27 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
     const int head_bytes = (int)(a.l_q * D * 2);
     const int32_t tiles_per_head = (int32_t)((a.l_q + QBC - 1) / QBC);
-    const int32_t n_tiles = tiles_per_head * a.group;
-    // Tile t: query head g*group + t / tiles_per_head, rows (t % tiles_per_head) * QBC ...
+    // Causal: only queries at or after a key's position see it; query tiles from s_min on
+    // hold all the queries that see a key of this work-group; fq is the first query that
+    // sees this lane's key (positions grow with the local index in every layout).
+    const CausalMap cmap{a.layout, a.rank, a.n_kblocks, kblk};
+    int32_t s_min = 0, fq = 0;
+    if constexpr (CAUSAL) {
+        const int32_t last = kblk - 1;
+        s_min = __builtin_amdgcn_readfirstlane(cmap.first_query(cmap.pos(j, u * KBR)) / QBC);
+        fq = cmap.first_query(cmap.pos(j, bl < last ? bl : last));
+    }
+    const int32_t act_per_head = tiles_per_head - s_min;
+    const int32_t n_tiles = act_per_head * a.group;
+    if (n_tiles == 0) return;  // no query of this share sees these keys (uniform)
+    // Tile t: query head g*group + t / act_per_head, rows (s_min + t % act_per_head) * QBC
+    auto tile_of = [&](int32_t t, int32_t &hh) {
+        hh = t / act_per_head;
+        return s_min + (t - hh * act_per_head);
+    };
     auto load = [&](int32_t t, int buf) {
-        const int32_t hh = t / tiles_per_head, s = t - hh * tiles_per_head;
+        int32_t hh;
+        const int32_t s = tile_of(t, hh);
         const int64_t bh = (int64_t)b * a.H + (int64_t)g * a.group + hh;
         const int64_t r0 = (int64_t)s * QBC;
         const int64_t left = a.l_q - r0;
@@ -381,14 +483,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
             }
         }
     };
-    // P and dS of tile t; rows past the end of the block get P = 0.  Packed in the
-    // contraction order of the gradient products (operand c4: queries
-    // 16 c4 + 8 (j/4) + 4 hf + j%4 = elements 8 (c4%2) + j of block c4/2).
-    auto softmax = [&](int buf, int32_t t, const f32x16 *sc, const f32x16 *dq, bf16x8 *pp,
-                       bf16x8 *dsp) {
-        const int32_t s_idx = t % tiles_per_head;
+    // P and dS of tile t: rows past the end of the block get P = 0 and, with MK == 2
+    // (causal), so do queries before this lane's first query fq.  Packed in the contraction
+    // order of the gradient products (operand c4: queries 16 c4 + 8 (j/4) + 4 hf + j%4 =
+    // elements 8 (c4%2) + j of block c4/2).
+    auto softmax = [&](auto mk, int buf, int32_t t, const f32x16 *sc, const f32x16 *dq,
+                       bf16x8 *pp, bf16x8 *dsp) {
+        constexpr int MK = decltype(mk)::value;
+        int32_t hh;
+        const int32_t s_idx = tile_of(t, hh);
         const int64_t left = a.l_q - (int64_t)s_idx * QBC;
         const int qlim = (left < QBC ? (int)left : QBC) - 4 * hf;  // valid query rows
+        const int qthr = fq - s_idx * QBC - 4 * hf;                // first seeing query
         const f32x2 *w = Wt[buf];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
@@ -404,7 +510,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * j4 + e, i = 8 * (c4 & 1) + j;
                     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c4 >> 1][i], c, -Lq[e]));
-                    if (q0 + e >= qlim) p = 0.f;
+                    if (MK >= 1 && q0 + e >= qlim) p = 0.f;
+                    if (MK == 2 && q0 + e < qthr) p = 0.f;
                     pp[c4][j] = (bf16)p;
                     dsp[c4][j] = (bf16)(p * (dq[c4 >> 1][i] - Dq[e]));
                 }
@@ -442,7 +549,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int nnb = nb == 2 ? 0 : nb + 1;     // tile t + 2 (held tile t - 1)
         if (t + 2 < n_tiles) load(t + 2, nnb);
         bf16x8 pp[4], dsp[4];
-        softmax(buf, t, s, dp, pp, dsp);
+        // (Masking only the tiles that need it, behind a branch, spills at d = 128.)
+        softmax(std::integral_constant<int, CAUSAL ? 2 : 1>{}, buf, t, s, dp, pp, dsp);
         if (t + 1 < n_tiles) scores(nb, s, dp);
         grads(buf, pp, dsp);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // tile t + 2 landed (this wave's part)
@@ -471,7 +579,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t launch_all(const BwdArgs &a, const float *O, const void *dO, const float *m,
                       const float *l, int64_t rows, hipStream_t st) {
     const int64_t prep_blocks = (rows * 16 + 255) / 256;
@@ -479,12 +587,12 @@ hipError_t launch_all(const BwdArgs &a, const float *O, const void *dO, const fl
                        (const bf16 *)dO, m, l, (f32x2 *)a.ws, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(a.n_wg), dim3(64 * QW), 0, st, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(a.n_wg), dim3(64 * QW), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     BwdArgs k = a;
     k.n_wg = a.n_kv_wg;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(k.n_wg), dim3(64 * KW), 0, st, k);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(k.n_wg), dim3(64 * KW), 0, st, k);
     return hipGetLastError();
 }
 
@@ -495,8 +603,13 @@ int bwd_key_tile() { return KBR; }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, const float *O, const void *dO, const float *m,
                            const float *l, int64_t rows, int d, hipStream_t st) {
-    if (d == 128) return launch_all<128>(a, O, dO, m, l, rows, st);
-    if (d == 64) return launch_all<64>(a, O, dO, m, l, rows, st);
+    const bool causal = a.layout != kNoCausal;
+    if (d == 128)
+        return causal ? launch_all<128, true>(a, O, dO, m, l, rows, st)
+                      : launch_all<128, false>(a, O, dO, m, l, rows, st);
+    if (d == 64)
+        return causal ? launch_all<64, true>(a, O, dO, m, l, rows, st)
+                      : launch_all<64, false>(a, O, dO, m, l, rows, st);
     return hipErrorInvalidValue;
 }
 

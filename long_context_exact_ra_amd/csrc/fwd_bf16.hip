@@ -42,6 +42,7 @@
 //  * Work-group ids are remapped so each XCD (8 per chip, one L2 each) works on a
 //    contiguous range of (batch, head, query tile): the work-groups sharing a K/V
 //    head stream the same tiles through one L2 at about the same time.
+#include "causal_map.h"
 #include "ra_internal.h"
 
 namespace ra {
@@ -65,9 +66,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format,
 // no swizzle, no thread-id addressing; reads past num_records return zero.
 constexpr int kRsrcWord3 = 0x00020000;
-// Token layouts of a causal share (values of the public ra_layout).
-constexpr int32_t RA_LAYOUT_CONTIGUOUS_ = 0;
-constexpr int32_t RA_LAYOUT_STRIPED_ = 1;
 
 __device__ __forceinline__ int xcd_remap(int wg, int n) {
     const int per = n / 8, rem = n % 8;
@@ -112,44 +110,6 @@ struct TileCursor {
                 act = t < n_blocks ? act_of(t) : 0;
             } while (t < n_blocks && act == 0);
         }
-    }
-};
-
-// Causal mask of a share (slowleelab "Ring Attention" page, 4.5 limitation 2: a query
-// attends only to keys at or before its own position).  Member r's local token x sits
-// at position r*l + x (contiguous), x*N + r (striped) or, with h = l/2, r*h + x for
-// x < h and (2N-1-r)*h + (x-h) after (zigzag).  allowed(a, j, b0) is the number of keys
-// b0, b0+1, ... of block j that local query a may attend to (any sign; only its
-// clamp to [0, 64] matters).  A 64-key tile never straddles a zigzag half-block.
-struct CausalMap {
-    int32_t layout, rank, N, l;
-    __device__ __forceinline__ int32_t qpos(int32_t a) const {  // contiguous and zigzag
-        if (layout == RA_LAYOUT_CONTIGUOUS_) return rank * l + a;
-        const int32_t hl = l >> 1;
-        return a < hl ? rank * hl + a : (2 * N - 1 - rank) * hl + (a - hl);
-    }
-    __device__ __forceinline__ int32_t kpos(int32_t j, int32_t b) const {
-        if (layout == RA_LAYOUT_CONTIGUOUS_) return j * l + b;
-        const int32_t hl = l >> 1;
-        return b < hl ? j * hl + b : (2 * N - 1 - j) * hl + (b - hl);
-    }
-    __device__ __forceinline__ int32_t allowed(int32_t a, int32_t j, int32_t b0) const {
-        // striped: x*N + j <= a*N + r  <=>  x <= a - (j > r)
-        if (layout == RA_LAYOUT_STRIPED_) return a - (j > rank ? 1 : 0) - b0 + 1;
-        return qpos(a) - kpos(j, b0) + 1;
-    }
-    // Tiles of block j that hold a key some query up to local index a_max may attend to.
-    __device__ __forceinline__ int32_t active_tiles(int32_t j, int32_t a_max,
-                                                    int32_t tiles_per_blk) const {
-        auto prefix = [](int32_t keys, int32_t cap) {  // tiles covering keys 0..keys-1
-            return keys <= 0 ? 0 : min(cap, (keys + BC - 1) / BC);
-        };
-        if (layout == RA_LAYOUT_STRIPED_)
-            return prefix(a_max - (j > rank ? 1 : 0) + 1, tiles_per_blk);
-        const int32_t q = qpos(a_max);  // positions grow with the local index
-        if (layout == RA_LAYOUT_CONTIGUOUS_) return prefix(q - j * l + 1, tiles_per_blk);
-        const int32_t hl = l >> 1, ht = hl / BC;
-        return prefix(q - j * hl + 1, ht) + prefix(q - (2 * N - 1 - j) * hl + 1, ht);
     }
 };
 
@@ -264,7 +224,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     const int32_t a_max = (int32_t)((a.l_q < a_end ? a.l_q : a_end) - 1);
     auto act_of = [&](int32_t t) -> int32_t {
         if constexpr (!CAUSAL) return tiles_per_blk;
-        else return cmap.active_tiles((int32_t)ring_block(a.rank, t, a.n_blocks), a_max,
+        else return cmap.active_tiles((int32_t)ring_block(a.rank, t, a.n_blocks), a_max, BC,
                                       tiles_per_blk);
     };
     int32_t n_tiles = tiles_per_blk * a.n_blocks;

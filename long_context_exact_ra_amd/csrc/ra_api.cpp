@@ -137,6 +137,65 @@ int share_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, in
     return launch_fwd(a, B, d, dtype, ra::MODE_SHARE, (hipStream_t)stream);
 }
 
+// Shared by ra_share_backward (layout kNoCausal) and ra_causal_share_backward.
+int backward_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, int32_t d,
+                    int32_t B, int32_t dtype, int32_t layout, const void *Q_i, const void *K,
+                    const void *V, const float *O, const void *dO, const float *m,
+                    const float *l, float scale, float *dQ, float *dK, float *dV,
+                    void *workspace, void *stream) {
+    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
+        !heads_ok(B, H, H_kv, d, dtype) || !scale_ok(scale))
+        return RA_EINVAL;
+    if (L == 0) return RA_OK;
+    if (!ptr_ok(Q_i) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(O) || !ptr_ok(dO) || !ptr_ok(m) ||
+        !ptr_ok(l) || !ptr_ok(dQ) || !ptr_ok(dK) || !ptr_ok(dV) || !ptr_ok(workspace))
+        return RA_EINVAL;
+    if (dtype != RA_BF16) return RA_ENOTSUP;  // the backward kernels take bf16 inputs
+    const int64_t lq = L / N;
+    if (!head_range_ok(dtype, L, d) || !head_range_ok(dtype, lq, d) ||
+        lq > (int64_t)INT32_MAX / 8)  // one head's statistics through a 32-bit buffer range
+        return RA_ENOTSUP;
+    const bool causal = layout != ra::kNoCausal;
+    const int64_t kblk = causal ? lq : L;
+    const int64_t nkb = causal ? N : 1;
+    const int64_t qt = (lq + ra::bwd_query_tile() - 1) / ra::bwd_query_tile();
+    const int64_t kpb = (kblk + ra::bwd_key_tile() - 1) / ra::bwd_key_tile();
+    const int64_t kt = kpb * nkb;
+    if (qt * B * H > INT32_MAX || kt * B * H_kv > INT32_MAX) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    ra::BwdArgs a{};
+    a.Q = Q_i;
+    a.K = K;
+    a.V = V;
+    a.dO = dO;
+    a.ws = (float *)workspace;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.l_q = lq;
+    a.L = L;
+    a.kv_head_stride = L * d;
+    a.kv_batch_stride = (int64_t)H_kv * L * d;
+    a.H = H;
+    a.H_kv = H_kv;
+    a.group = H / H_kv;
+    a.n_qtiles = (int32_t)qt;
+    a.n_wg = (int32_t)(qt * B * H);
+    a.n_ktiles = (int32_t)kt;
+    a.n_kv_wg = (int32_t)(kt * B * H_kv);
+    a.n_kblocks = (int32_t)nkb;
+    a.kblk_rows = kblk;
+    a.n_ktiles_blk = (int32_t)kpb;
+    a.layout = layout;
+    a.rank = rank;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipStream_t st = (hipStream_t)stream;
+    return after_launch(
+        ra::launch_bwd_bf16(a, O, dO, m, l, (int64_t)B * H * lq, d, st), st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,48 +333,23 @@ int ra_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_k
                       const float *O, const void *dO, const float *m, const float *l,
                       float scale, float *dQ, float *dK, float *dV, void *workspace,
                       void *stream) {
-    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
-        !heads_ok(B, H, H_kv, d, dtype) || !scale_ok(scale))
+    return backward_launch(rank, N, L, H, H_kv, d, B, dtype, ra::kNoCausal, Q_i, K, V, O, dO,
+                           m, l, scale, dQ, dK, dV, workspace, stream);
+}
+
+int ra_causal_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                             int32_t d, int32_t B, int32_t dtype, int32_t layout,
+                             const void *Q_i, const void *K, const void *V, const float *O,
+                             const void *dO, const float *m, const float *l, float scale,
+                             float *dQ, float *dK, float *dV, void *workspace, void *stream) {
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED &&
+        layout != RA_LAYOUT_ZIGZAG)
         return RA_EINVAL;
-    if (L == 0) return RA_OK;
-    if (!ptr_ok(Q_i) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(O) || !ptr_ok(dO) || !ptr_ok(m) ||
-        !ptr_ok(l) || !ptr_ok(dQ) || !ptr_ok(dK) || !ptr_ok(dV) || !ptr_ok(workspace))
+    // Zigzag: each half-block must be whole 64-row tiles (as in the forward pass).
+    if (layout == RA_LAYOUT_ZIGZAG && N >= 1 && L >= 0 && L % N == 0 && (L / N) % 128 != 0)
         return RA_EINVAL;
-    if (dtype != RA_BF16) return RA_ENOTSUP;  // the backward kernels take bf16 inputs
-    const int64_t lq = L / N;
-    if (!head_range_ok(dtype, L, d) || !head_range_ok(dtype, lq, d) ||
-        lq > (int64_t)INT32_MAX / 8)  // one head's statistics through a 32-bit buffer range
-        return RA_ENOTSUP;
-    ra::BwdArgs a{};
-    const int64_t qt = (lq + ra::bwd_query_tile() - 1) / ra::bwd_query_tile();
-    const int64_t kt = (L + ra::bwd_key_tile() - 1) / ra::bwd_key_tile();
-    if (qt * B * H > INT32_MAX || kt * B * H_kv > INT32_MAX) return RA_ENOTSUP;
-    int rc = check_device();
-    if (rc != RA_OK) return rc;
-    a.Q = Q_i;
-    a.K = K;
-    a.V = V;
-    a.dO = dO;
-    a.ws = (float *)workspace;
-    a.dQ = dQ;
-    a.dK = dK;
-    a.dV = dV;
-    a.l_q = lq;
-    a.L = L;
-    a.kv_head_stride = L * d;
-    a.kv_batch_stride = (int64_t)H_kv * L * d;
-    a.H = H;
-    a.H_kv = H_kv;
-    a.group = H / H_kv;
-    a.n_qtiles = (int32_t)qt;
-    a.n_wg = (int32_t)(qt * B * H);
-    a.n_ktiles = (int32_t)kt;
-    a.n_kv_wg = (int32_t)(kt * B * H_kv);
-    a.scale = scale;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    hipStream_t st = (hipStream_t)stream;
-    return after_launch(
-        ra::launch_bwd_bf16(a, O, dO, m, l, (int64_t)B * H * lq, d, st), st);
+    return backward_launch(rank, N, L, H, H_kv, d, B, dtype, layout, Q_i, K, V, O, dO, m, l,
+                           scale, dQ, dK, dV, workspace, stream);
 }
 
 const char *ra_strerror(int status) {

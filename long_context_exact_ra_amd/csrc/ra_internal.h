@@ -62,6 +62,14 @@ struct BwdArgs {
     int32_t n_wg;       // dQ work-groups
     int32_t n_ktiles;   // dK/dV: key tiles per (batch, kv head)
     int32_t n_kv_wg;    // dK/dV work-groups
+    // Key tiling: n_kblocks blocks of kblk_rows keys each (block j = rows j*kblk_rows ...);
+    // tiles never straddle two blocks.  A causal share has one block per ring member
+    // (n_kblocks = N, kblk_rows = l_q); otherwise the keys are one block of L rows.
+    int32_t n_kblocks;
+    int64_t kblk_rows;
+    int32_t n_ktiles_blk;  // dK/dV key tiles per block
+    int32_t layout;        // ra_layout of a causal share, or kNoCausal
+    int32_t rank;          // ring member whose queries these are (causal only)
     float scale;
     float scale_log2;
 };

@@ -71,6 +71,9 @@ def load():
         "ra_causal_pairs": (i64, [i32, i32, i64, i32]),
         "ra_share_backward": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, i32, vp, vp,
                                              vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp]),
+        "ra_causal_share_backward": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, i32,
+                                                    i32, vp, vp, vp, vp, vp, vp, vp, f32, vp,
+                                                    vp, vp, vp, vp]),
         "ra_share_backward_workspace": (i64, [i32, i32, i64]),
         "ra_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "ra_last_hip_error": (ctypes.c_int, []),
@@ -86,7 +89,8 @@ def load():
 def exported_symbols() -> list[str]:
     return ["ra_ring_block", "ra_ring_schedule", "ra_kv_head", "ra_state_init", "ra_step",
             "ra_finalize", "ra_share_forward", "ra_causal_share_forward", "ra_causal_pairs",
-            "ra_share_backward", "ra_share_backward_workspace", "ra_strerror",
+            "ra_share_backward", "ra_causal_share_backward", "ra_share_backward_workspace",
+            "ra_strerror",
             "ra_last_hip_error"]
 
 
@@ -273,11 +277,8 @@ def causal_pairs(rank: int, N: int, L: int, layout) -> int:
     return n
 
 
-def share_backward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int, Q_i, K, V, O,
-                   dO, m, l, scale: float, dQ, dK, dV, workspace=None, stream=None):
-    """Gradients of rank `rank`'s share (see ra_share_backward in ra.h): dQ is written,
-    dK and dV are added to.  `workspace` (a uint8 device tensor of
-    ra_share_backward_workspace bytes) is allocated here when not given."""
+def _backward(rank, N, L, H, H_kv, d, B, layout, Q_i, K, V, O, dO, m, l, scale, dQ, dK, dV,
+              workspace, stream):
     if N < 1 or L % N != 0:
         raise ValueError("L must be a multiple of N >= 1")
     lq = L // N
@@ -297,8 +298,31 @@ def share_backward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int,
         workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=Q_i.device)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
-    _check(load().ra_share_backward(
-        rank, N, L, H, H_kv, d, B, _dtype_code(Q_i), _dev(Q_i, "Q_i"), _dev(K, "K"),
-        _dev(V, "V"), _dev(O, "O"), _dev(dO, "dO"), _dev(m, "m"), _dev(l, "l"), float(scale),
-        _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"), _dev(workspace, "workspace"),
-        _stream(stream)), "ra_share_backward")
+    args = (_dev(Q_i, "Q_i"), _dev(K, "K"), _dev(V, "V"), _dev(O, "O"), _dev(dO, "dO"),
+            _dev(m, "m"), _dev(l, "l"), float(scale), _dev(dQ, "dQ"), _dev(dK, "dK"),
+            _dev(dV, "dV"), _dev(workspace, "workspace"), _stream(stream))
+    if layout is None:
+        _check(load().ra_share_backward(rank, N, L, H, H_kv, d, B, _dtype_code(Q_i), *args),
+               "ra_share_backward")
+    else:
+        _check(load().ra_causal_share_backward(rank, N, L, H, H_kv, d, B, _dtype_code(Q_i),
+                                               _layout_code(layout), *args),
+               "ra_causal_share_backward")
+
+
+def share_backward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int, Q_i, K, V, O,
+                   dO, m, l, scale: float, dQ, dK, dV, workspace=None, stream=None):
+    """Gradients of rank `rank`'s share (see ra_share_backward in ra.h): dQ is written,
+    dK and dV are added to.  `workspace` (a uint8 device tensor of
+    ra_share_backward_workspace bytes) is allocated here when not given."""
+    _backward(rank, N, L, H, H_kv, d, B, None, Q_i, K, V, O, dO, m, l, scale, dQ, dK, dV,
+              workspace, stream)
+
+
+def causal_share_backward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int,
+                          layout, Q_i, K, V, O, dO, m, l, scale: float, dQ, dK, dV,
+                          workspace=None, stream=None):
+    """Gradients of rank `rank`'s causal share under `layout` (see ra_causal_share_backward
+    in ra.h); arguments as in share_backward."""
+    _backward(rank, N, L, H, H_kv, d, B, layout, Q_i, K, V, O, dO, m, l, scale, dQ, dK, dV,
+              workspace, stream)

@@ -317,17 +317,22 @@ def share_backward(Q, K, V, dO, scale, rank: int = 0, N: int = 1, layout: str | 
     return dQ, dK, dV
 
 
-def share_backward_rows(Q, K, V, dO, scale, heads, q_rows, k_rows, chunk: int = 512):
+def share_backward_rows(Q, K, V, dO, scale, heads, q_rows, k_rows, chunk: int = 512,
+                        rank: int = 0, N: int = 1, layout: str | None = None):
     """Sampled gradients for large shares, without materialising l x L per head at once.
     heads: list of (b, h) query heads; q_rows / k_rows: local query rows and key rows to
     report for each of them.  Returns, per head, (dQ[q_rows] [nq, d], dK_part[k_rows],
     dV_part[k_rows]) where the K/V parts are this query head's contribution only.
-    Same formulas as share_backward, evaluated in query chunks: the softmax statistics
-    of every query row are computed first (they are what the backward pass reuses)."""
+    Same formulas as share_backward, evaluated in query chunks (with `layout`, each
+    chunk's scores are restricted to the admissible keys as in causal_share)."""
     q_all, k_all, v_all, do_all = Q, K, V, dO
     H = q_all.shape[1]
     H_kv = k_all.shape[1]
     g = H // H_kv
+    qpos = kpos = None
+    if layout is not None:
+        qpos = token_positions(layout, rank, N, q_all.shape[2])
+        kpos = layout_positions(layout, N, k_all.shape[2])
     out = []
     for (b, h) in heads:
         q = _f64(q_all[b, h])
@@ -343,6 +348,8 @@ def share_backward_rows(Q, K, V, dO, scale, heads, q_rows, k_rows, chunk: int = 
         for c0 in range(0, l, chunk):
             c1 = min(l, c0 + chunk)
             S = scale * (q[c0:c1] @ k.T)
+            if qpos is not None:
+                S = np.where(kpos[None, :] <= qpos[c0:c1, None], S, -np.inf)
             P = np.exp(S - S.max(axis=1, keepdims=True))
             P /= P.sum(axis=1, keepdims=True)
             dP = do[c0:c1] @ v.T

@@ -203,3 +203,51 @@ def test_causal_share_rejects(kw):
 def test_causal_share_limits_and_noop():
     assert _causal(L=0, Q=None, K=None, V=None, O=None) == ra.RA_OK
     assert _causal(N=8, L=1 << 23, d=128) == ra.RA_ENOTSUP
+
+
+# ------------------------------------------------------------------ backward
+
+def _backward(causal=False, **kw):
+    args = dict(rank=3, N=8, L=8 * 128, H=4, H_kv=2, d=128, B=1, dtype=ra.RA_BF16, layout=0,
+                Q=P, K=P, V=P, O=P2, dO=P, m=P2, l=P2, scale=0.088, dQ=P2, dK=P2, dV=P2,
+                ws=P2, stream=None)
+    args.update(kw)
+    tail = (args["Q"], args["K"], args["V"], args["O"], args["dO"], args["m"], args["l"],
+            args["scale"], args["dQ"], args["dK"], args["dV"], args["ws"], args["stream"])
+    head = (args["rank"], args["N"], args["L"], args["H"], args["H_kv"], args["d"], args["B"],
+            args["dtype"])
+    lib = ra.load()
+    if causal:
+        return lib.ra_causal_share_backward(*head, args["layout"], *tail)
+    return lib.ra_share_backward(*head, *tail)
+
+
+BACKWARD_REJECTS = [
+    dict(N=0), dict(rank=-1), dict(rank=8), dict(L=8 * 128 + 1), dict(L=-8), dict(H=5),
+    dict(H_kv=0), dict(d=96), dict(B=0), dict(dtype=7), dict(scale=0.0),
+    dict(scale=float("nan")), dict(Q=None), dict(K=None), dict(V=None), dict(O=None),
+    dict(dO=None), dict(m=None), dict(l=None), dict(dQ=None), dict(dK=None), dict(dV=None),
+    dict(ws=None), dict(O=MIS), dict(dQ=MIS), dict(ws=MIS),
+]
+
+
+@pytest.mark.parametrize("kw", BACKWARD_REJECTS)
+def test_share_backward_rejects(kw):
+    assert _backward(**kw) == ra.RA_EINVAL
+
+
+@pytest.mark.parametrize("kw", BACKWARD_REJECTS + [
+    dict(layout=3), dict(layout=-1), dict(layout=2, L=8 * 64), dict(layout=2, L=8 * 192)])
+def test_causal_share_backward_rejects(kw):
+    assert _backward(causal=True, **kw) == ra.RA_EINVAL
+
+
+def test_backward_limits_and_noop():
+    for causal in (False, True):
+        assert _backward(causal, L=0, Q=None, K=None, V=None, dQ=None) == ra.RA_OK
+        # fp32 inputs: the backward kernels take bf16 only
+        assert _backward(causal, dtype=ra.RA_F32) == ra.RA_ENOTSUP
+        assert _backward(causal, N=8, L=1 << 23, d=128) == ra.RA_ENOTSUP
+    lib = ra.load()
+    assert lib.ra_share_backward_workspace(2, 3, 100) == 8 * 2 * 3 * 100
+    assert lib.ra_share_backward_workspace(-1, 3, 100) == -ra.RA_EINVAL

@@ -104,3 +104,21 @@ def test_sampled_rows_agree_with_the_dense_gradient():
     only = oracle.share_backward(Q[:, 2:4], K[:, 1:2], V[:, 1:2], dO[:, 2:4], 0.3)
     np.testing.assert_allclose(dK_h[2][0] + oracle.share_backward_rows(
         Q, K, V, dO, 0.3, [(0, 3)], [], k_rows)[0][1], only[1][0, 0, k_rows], atol=1e-12)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_sampled_causal_rows_agree_with_the_dense_causal_gradient(layout):
+    """The chunked, sampled form with a layout against the dense masked gradient (itself
+    pinned to autograd and finite differences above), one query head per K/V head so the
+    key-row parts are the whole gradient."""
+    rng = np.random.default_rng(17)
+    N, l, rank = 4, 32, 2
+    Q, K, V, dO = _draw(rng, 1, 2, 2, l, N * l, 8)
+    dQ, dK, dV = oracle.share_backward(Q, K, V, dO, 0.3, rank, N, layout)
+    q_rows, k_rows = [0, 9, 16, 31], [0, 40, 64, 77, 100, 127]
+    res = oracle.share_backward_rows(Q, K, V, dO, 0.3, [(0, 0), (0, 1)], q_rows, k_rows,
+                                     chunk=8, rank=rank, N=N, layout=layout)
+    for h, (gq, gk, gv) in enumerate(res):
+        np.testing.assert_allclose(gq, dQ[0, h, q_rows], atol=1e-12)
+        np.testing.assert_allclose(gk, dK[0, h, k_rows], atol=1e-12)
+        np.testing.assert_allclose(gv, dV[0, h, k_rows], atol=1e-12)
