@@ -29,6 +29,11 @@ share_backward(...), share_backward_rows(...)
     the backward pass recomputes the scores from the stored output and softmax
     statistics instead of storing the attention matrix; the gradient itself is that of
     softmax(scale Q K^T) V).  fp64 numpy, every matrix materialised.
+fp8 (submodule)
+    OCP E4M3 encoding, block quantization of Q/K (64-row blocks) and V (per channel,
+    stored tile-transposed), and the share over such inputs as the plain definition on
+    the dequantized values (aliyun page, FlashAttention-3: FP8 products with block
+    quantization).
 online_step(...)
     One merge of a K/V block into the running state (O_acc, m, l), in the order of
     the per-step pseudocode on the slowleelab page (section 4.3), fp64 numpy, with
@@ -51,6 +56,7 @@ _lib = None
 
 F32 = 0
 BF16 = 1
+F64 = 2
 
 
 def build(force: bool = True) -> str:
@@ -113,12 +119,15 @@ def kv_head(h: int, H: int, H_kv: int) -> int:
 
 
 def _raw(a: np.ndarray):
-    """(dtype code, contiguous buffer) of an fp32 array or a bf16-bits uint16 array."""
+    """(dtype code, contiguous buffer) of an fp32 array, a bf16-bits uint16 array or an
+    fp64 array."""
     if a.dtype == np.float32:
         return F32, np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return BF16, np.ascontiguousarray(a)
-    raise TypeError("inputs must be float32 arrays or uint16 arrays holding bf16 bits")
+    if a.dtype == np.float64:
+        return F64, np.ascontiguousarray(a)
+    raise TypeError("inputs must be float32, float64, or uint16 arrays holding bf16 bits")
 
 
 def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
@@ -126,7 +135,8 @@ def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
                    qpos=None, kpos=None):
     """The plain definition over the listed key ranges, for the listed query rows.
 
-    Q: [B, H, l_q, d]; K, V: [B, H_kv, L, d]; all float32, or all uint16 bf16 bits.
+    Q: [B, H, l_q, d]; K, V: [B, H_kv, L, d]; all float32, all float64, or all uint16
+    bf16 bits.
     rows: flat indices (b*H + h)*l_q + r (default: every row).
     key_ranges: list of (lo, hi) half-open key ranges (default: all L keys).
     scale: the fp32 scale the GPU uses, widened to fp64 here.

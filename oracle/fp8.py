@@ -1,0 +1,165 @@
+"""FP8 (OCP E4M3) inputs for a share: block quantization and the attention it defines.
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: only the test suite, the smoke
+check and the CPU-baseline leg of the benchmark use it.
+
+FlashAttention-3 runs the forward products on FP8 matrix units and limits the precision
+lost in the conversion with block quantization (aliyun FlashAttention explainer,
+section 2, the FlashAttention-3 paragraph on low-precision GEMMs).  The pages fix
+neither the FP8 format nor the block shapes; the readings taken here are:
+
+* Format: OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits with bias 7, 3 mantissa
+  bits; exponent 0 holds the subnormals m/8 * 2^-6; S.1111.111 is NaN; there are no
+  infinities and the largest finite value is 448.  Encoding rounds to nearest, ties to
+  even; magnitudes at or beyond 464 (half-way to the next, non-existent step) give NaN.
+* Blocks: Q and K get one scale per 64-row block of each member's block of rows (a K/V
+  tile, or a query tile); V gets one scale per channel (head-dim column) over the
+  whole sequence, which can be applied once to the output.
+* Scale: descale = max(float32(amax / 448), 2^-126) per block, with amax the largest
+  magnitude in the block; a value x is stored as encode(float32(x * float32(1 /
+  descale))) and stands for descale * decode(code).  All of that arithmetic is fp32
+  with round-to-nearest, as written.
+* V is stored tile-transposed: for each member block s and 64-row tile u, a [d, 64]
+  byte matrix whose column r is row s*seg + 64u + r (zero past the block end).
+
+The share over such inputs is the plain definition of attention over the dequantized
+values (fp64 products descale * decode(code) are exact), evaluated by the same C code as
+the bf16 share.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+FLT_MIN = np.float32(2.0 ** -126)
+TILE = 64  # rows per scale block of Q and K, keys per stored V tile
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """fp64 value of each E4M3 code (uint8); NaN for the two NaN codes."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 code (uint8) of each float32 value, round to nearest, ties to even."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)  # exact
+    a = np.where(np.isfinite(a), a, 1e9)  # non-finite inputs take the NaN code below
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int64)
+    # subnormal range: multiples of 2^-9 below 2^-6 (q == 8 is the smallest normal)
+    q_sub = np.rint(a * 2.0 ** 9).astype(np.int64)
+    # normal range: a = (1 + f) 2^e with f in [0, 1); 8 f rounded to an integer
+    frac, ex = np.frexp(np.where(a > 0, a, 1.0))  # a = frac * 2^ex, frac in [0.5, 1)
+    e = ex.astype(np.int64) - 1
+    q = np.rint((frac * 2.0 - 1.0) * 8.0).astype(np.int64)
+    carry = q == 8
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 0, q)
+    normal = (e + 7) * 8 + q
+    over = (e > 8) | ((e == 8) & (q == 7))
+    code = np.where(a < 2.0 ** -6, q_sub, np.where(over, 0x7F, normal))
+    return (sign | code).astype(np.uint8)
+
+
+def block_descale(amax) -> np.ndarray:
+    """max(float32(amax / 448), 2^-126), elementwise, float32."""
+    amax = np.asarray(amax, dtype=np.float32)
+    return np.maximum(amax / np.float32(E4M3_MAX), FLT_MIN).astype(np.float32)
+
+
+def _quantize(x32: np.ndarray, descale: np.ndarray) -> np.ndarray:
+    inv = (np.float32(1.0) / descale).astype(np.float32)
+    return e4m3_encode((x32 * inv).astype(np.float32))
+
+
+def _f32(x) -> np.ndarray:
+    """bf16 bits (uint16) or float32 values as float32."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    if x.dtype == np.float32:
+        return x
+    raise TypeError("expected bf16 bits (uint16) or float32")
+
+
+def quantize_rows(x, n_seg: int, seg: int):
+    """Per-block quantization of x [B, Hx, n_seg*seg, d] (bf16 bits or float32): blocks
+    of 64 rows inside each of the n_seg segments of seg rows (the last block of a
+    segment may be shorter).  Returns (codes uint8 [B, Hx, n_seg*seg, d], descale
+    float32 [B, Hx, n_seg, ceil(seg/64)])."""
+    x32 = _f32(x)
+    B, Hx, R, d = x32.shape
+    if R != n_seg * seg:
+        raise ValueError("rows must be n_seg * seg")
+    T = -(-seg // TILE)
+    codes = np.empty(x32.shape, dtype=np.uint8)
+    descale = np.empty((B, Hx, n_seg, T), dtype=np.float32)
+    for s in range(n_seg):
+        for u in range(T):
+            r0 = s * seg + u * TILE
+            r1 = min(r0 + TILE, (s + 1) * seg)
+            blk = x32[:, :, r0:r1, :]
+            ds = block_descale(np.abs(blk).max(axis=(2, 3)))  # [B, Hx]
+            descale[:, :, s, u] = ds
+            codes[:, :, r0:r1, :] = _quantize(blk, ds[:, :, None, None])
+    return codes, descale
+
+
+def quantize_vt(x, n_seg: int, seg: int):
+    """Per-channel quantization of x [B, Hx, n_seg*seg, d] over all rows, stored
+    tile-transposed.  Returns (codes uint8 [B, Hx, n_seg, T, d, 64], descale float32
+    [B, Hx, d]), T = ceil(seg/64); columns past a segment's end hold code 0."""
+    x32 = _f32(x)
+    B, Hx, R, d = x32.shape
+    if R != n_seg * seg:
+        raise ValueError("rows must be n_seg * seg")
+    T = -(-seg // TILE)
+    descale = block_descale(np.abs(x32).max(axis=2))  # [B, Hx, d]
+    q = _quantize(x32, descale[:, :, None, :])  # [B, Hx, R, d]
+    codes = np.zeros((B, Hx, n_seg, T, d, TILE), dtype=np.uint8)
+    for s in range(n_seg):
+        for u in range(T):
+            r0 = s * seg + u * TILE
+            r1 = min(r0 + TILE, (s + 1) * seg)
+            codes[:, :, s, u, :, : r1 - r0] = np.swapaxes(q[:, :, r0:r1, :], 2, 3)
+    return codes, descale
+
+
+def dequantize_rows(codes, descale, seg: int) -> np.ndarray:
+    """fp64 values of quantize_rows' output (exact)."""
+    B, Hx, R, d = codes.shape
+    rows = np.arange(R)
+    s, u = rows // seg, (rows % seg) // TILE
+    ds = np.asarray(descale, dtype=np.float64)[:, :, s, u]  # [B, Hx, R]
+    return e4m3_decode(codes) * ds[:, :, :, None]
+
+
+def dequantize_vt(codes, descale, seg: int) -> np.ndarray:
+    """fp64 values [B, Hx, n_seg*seg, d] of quantize_vt's output (exact)."""
+    B, Hx, n_seg, T, d, _ = codes.shape
+    R = n_seg * seg
+    rows = np.arange(R)
+    s, u, r = rows // seg, (rows % seg) // TILE, (rows % seg) % TILE
+    rows_major = np.swapaxes(codes, 4, 5)  # [B, Hx, n_seg, T, 64, d]
+    vals = e4m3_decode(rows_major[:, :, s, u, r, :])  # [B, Hx, R, d]
+    return vals * np.asarray(descale, dtype=np.float64)[:, :, None, :]
+
+
+def share_fp8(Q8, q_descale, K8, k_descale, V8t, v_descale, scale, rank: int, N: int,
+              rows=None, nthreads=None):
+    """Rank `rank`'s share over FP8 inputs: Q8 [B, H, l, d] with q_descale
+    [B, H, 1, ceil(l/64)]; K8 [B, H_kv, L, d] with k_descale [B, H_kv, N, ceil(l/64)];
+    V8t [B, H_kv, N, ceil(l/64), d, 64] with v_descale [B, H_kv, d].  The plain
+    definition over the dequantized values; returns (O, M, Z) as attention_rows."""
+    from . import share
+    l = Q8.shape[2]
+    Qd = dequantize_rows(Q8, q_descale, l)
+    Kd = dequantize_rows(K8, k_descale, l)
+    Vd = dequantize_vt(V8t, v_descale, l)
+    return share(Qd, Kd, Vd, scale, rank, N, rows=rows, nthreads=nthreads)

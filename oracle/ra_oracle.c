@@ -26,7 +26,8 @@
  *     Z   = sum_k p_k
  *     O   = (sum_k p_k * V[b,g,k,:]) / Z
  * All arithmetic is fp64 and every score of the row is materialised.  Inputs are
- * read as their stored bits (fp32 or bf16; both widen to fp64 exactly).
+ * read as their stored bits (fp32 or bf16, both widened to fp64 exactly, or fp64
+ * values such as dequantized fp8 inputs, which fp32 cannot hold exactly).
  *
  * Layouts (row-major): Q is [B, H, l_q, d]; K and V are [B, H_kv, L, d].
  */
@@ -40,11 +41,14 @@
 
 #define ORA_F32 0
 #define ORA_BF16 1
+#define ORA_F64 2
 
 static double widen(const void *base, int dtype, int64_t idx)
 {
     if (dtype == ORA_F32)
         return (double)((const float *)base)[idx];
+    if (dtype == ORA_F64)
+        return ((const double *)base)[idx];
     uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -70,7 +74,7 @@ int ra_oracle_rows_masked(int dtype, const void *Q, int64_t l_q, const void *K,
                           const int64_t *qpos, const int64_t *kpos, double *O, double *M,
                           double *Z, int nthreads)
 {
-    if ((dtype != ORA_F32 && dtype != ORA_BF16) || !Q || !K || !V || !rows || !O || !M ||
+    if ((dtype != ORA_F32 && dtype != ORA_BF16 && dtype != ORA_F64) || !Q || !K || !V || !rows || !O || !M ||
         !Z || l_q < 1 || L < 1 || B < 1 || H < 1 || H_kv < 1 || d < 1 || H % H_kv != 0 ||
         n_rows < 0 || n_ranges < 1 || !key_lo || !key_hi || (!qpos) != (!kpos))
         return 1;
