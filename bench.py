@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: 256 CU x 8192 FLOP/clk x 2.4 GHz
 KERNEL_SRC = os.path.join(ROOT, "long_context_exact_ra_amd", "csrc", "fwd_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_share_L128K_N8.json")
 
@@ -61,6 +62,8 @@ def parse():
                    help="time the share's backward pass (ra_share_backward) instead")
     p.add_argument("--causal-sweep", action="store_true",
                    help="time every member's causal share under each layout (balance data)")
+    p.add_argument("--fp8", action="store_true",
+                   help="time the share from FP8 (e4m3) inputs (ra_share_forward_fp8) instead")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -111,6 +114,35 @@ def main():
     scale = 1.0 / math.sqrt(w.d)
     O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
 
+    if args.fp8 and (args.backward or args.causal or args.step_path):
+        raise SystemExit("--fp8 times the non-causal forward share only")
+    extra = {}
+    if args.fp8:
+        T = ra.fp8_tiles(w.l)
+        u8, f32 = torch.uint8, torch.float32
+        Q8 = torch.empty((w.B, w.H, w.l, w.d), dtype=u8, device=dev)
+        qs = torch.empty((w.B, w.H, 1, T), dtype=f32, device=dev)
+        K8 = torch.empty((w.B, w.H_kv, w.L, w.d), dtype=u8, device=dev)
+        ks = torch.empty((w.B, w.H_kv, w.N, T), dtype=f32, device=dev)
+        V8 = torch.empty((w.B, w.H_kv, w.N, T, w.d, 64), dtype=u8, device=dev)
+        vs = torch.empty((w.B, w.H_kv, w.d), dtype=f32, device=dev)
+
+        def quantize():
+            ra.quantize_fp8("rows", qd, 1, Q8, qs)
+            ra.quantize_fp8("rows", kd, w.N, K8, ks)
+            ra.quantize_fp8("vt", vd, w.N, V8, vs)
+
+        quantize()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        quantize()
+        e1.record()
+        torch.cuda.synchronize()
+        qbytes = 2 * (qd.numel() + kd.numel() + vd.numel())  # bf16 read once (V: twice)
+        extra["quantize"] = {"ms": round(e0.elapsed_time(e1), 4),
+                             "input_GB": round(qbytes / 1e9, 3)}
+
     if args.backward:
         g = torch.Generator().manual_seed(w.seed + 99)
         dOd = torch.randn((w.B, w.H, w.l, w.d), generator=g).to(torch.bfloat16).to(dev)
@@ -129,7 +161,10 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     def step():
-        if args.backward and args.causal:
+        if args.fp8:
+            ra.share_forward_fp8(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, Q8, qs, K8, ks, V8,
+                                 vs, scale, O)
+        elif args.backward and args.causal:
             ra.causal_share_backward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, args.causal, qd,
                                      kd, vd, O, dOd, m_f, l_f, scale, dQ, dK, dV, ws)
         elif args.backward:
@@ -165,7 +200,6 @@ def main():
             flops *= 2.5
     tflops = flops / (ms * 1e-3) / 1e12
 
-    extra = {}
     if args.step_path and not args.causal and not args.backward:
         O_acc = torch.empty_like(O)
         m = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
@@ -190,14 +224,16 @@ def main():
         extra["step_path"] = {"ms": round(sp_ms, 4),
                               "tflops": round(flops / (sp_ms * 1e-3) / 1e12, 2)}
 
-    traffic = None if (args.causal or args.backward) else traffic_per_launch(name)
-    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic}
+    traffic = None if (args.causal or args.backward or args.fp8) else traffic_per_launch(name)
+    peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
 
     cpu_baseline = None
     parity = None
-    if args.backward and not args.no_cpu_baseline:
+    if args.fp8 and not args.no_cpu_baseline:
+        cpu_baseline, parity = fp8_cpu_baseline(w, q, k, v, O, scale, args)
+    elif args.backward and not args.no_cpu_baseline:
         cpu_baseline, parity = backward_cpu_baseline(w, q, k, v, dOd, dQ, scale, args)
     elif not args.no_cpu_baseline:
         import oracle
@@ -241,6 +277,8 @@ def main():
     metric = "ring-share attention TFLOP/s (bf16) + % of MFMA peak at L=128K, N=8"
     if args.causal:
         metric = f"causal ring-share attention TFLOP/s, useful pairs only ({args.causal} layout)"
+    if args.fp8:
+        metric = "ring-share attention TFLOP/s (fp8 e4m3 products) + % of fp8 MFMA peak"
     if args.backward:
         metric = "ring-share attention backward TFLOP/s (bf16; 2.5x forward FLOPs)"
         if args.causal:
@@ -257,13 +295,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if args.fp8 else "bf16",
         "data": "synthetic (seeded normal Q/K/V, resident in HBM)",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d, "L": w.L,
                    "N": w.N, "rank": w.rank, "l": w.l, "flops_per_step": flops,
                    **({"causal": args.causal} if args.causal else {}),
-                   **({"pass": "backward"} if args.backward else {})},
-        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                   **({"pass": "backward"} if args.backward else {}),
+                   **({"inputs": "fp8_e4m3, block-quantized"} if args.fp8 else {})},
+        "pct_of_peak": round(100 * tflops / peak, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity": parity,
@@ -302,6 +341,71 @@ def backward_cpu_baseline(w, q, k, v, dOd, dQ, scale, args):
              "sample": f"one head's backward statistics and {n} dQ rows "
                        f"({stat_flops:.3e} FLOP, {probe:.1f} s, fp64 numpy)"},
             {"rows": n, "max_abs_err": err, "ok": bool(err <= 2e-2 * np.abs(ref).max() + 1e-5)})
+
+
+def fp8_cpu_baseline(w, q, k, v, O, scale, args):
+    """The oracle's FP8 share (its own quantization of two heads' bf16 inputs, then
+    dequantization and the plain definition) on a bounded sample of those heads' rows;
+    the GPU's rows are checked against it with the derived FP8 bound."""
+    import numpy as np
+
+    import oracle
+    from oracle import fp8 as ofp8
+    from long_context_exact_ra_amd import synth
+    heads = [0, w.H // 2]
+    group = w.H // w.H_kv
+    codes = {}
+    for h in heads:
+        g = h // group
+        qh, kh, vh = (synth.to_oracle_array(x) for x in
+                      (q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1]))
+        codes[h] = (*ofp8.quantize_rows(qh, 1, w.l), *ofp8.quantize_rows(kh, w.N, w.l),
+                    *ofp8.quantize_vt(vh, w.N, w.l))
+    threads = oracle.max_threads()
+    # cost model from two probes: fixed (dequantization) + per row (attention)
+    t = time.perf_counter()
+    ofp8.share_fp8(*codes[heads[0]], scale, w.rank, w.N, rows=list(range(threads)))
+    t1 = time.perf_counter() - t
+    t = time.perf_counter()
+    ofp8.share_fp8(*codes[heads[0]], scale, w.rank, w.N, rows=list(range(4 * threads)))
+    t2 = time.perf_counter() - t
+    per_row = max((t2 - t1) / (3 * threads), 1e-6)
+    fixed = max(t1 - threads * per_row, 0.0)
+    per_head = int((args.cpu_seconds / len(heads) - fixed) / per_row)
+    per_head = min(max(per_head, threads), w.l)
+    g = np.random.default_rng(w.seed + 13)
+    t = time.perf_counter()
+    refs, picks = [], []
+    for h in heads:
+        rows = np.sort(g.choice(w.l, size=per_head, replace=False))
+        refs.append(ofp8.share_fp8(*codes[h], scale, w.rank, w.N, rows=rows)[0])
+        picks.append(rows)
+    cpu_s = time.perf_counter() - t
+    n = sum(len(p) for p in picks)
+    flops = 4.0 * w.L * w.d * n
+    import torch
+    worst, max_err, max_ref, n_bound = 0.0, 0.0, 0.0, 0
+    for h, rows, ref in zip(heads, picks, refs):
+        got = O[0, h][torch.tensor(rows, device=O.device)].double().cpu().numpy()
+        Q8, qs, K8, ks, V8, vs = codes[h]
+        chk = rows[:: max(1, len(rows) // 32)]  # the bound needs every score of a row
+        sel = np.searchsorted(rows, chk)
+        n_bound += len(chk)
+        bO, _, _ = ofp8.error_bounds(ofp8.dequantize_rows(Q8, qs, w.l),
+                                     ofp8.dequantize_rows(K8, ks, w.l),
+                                     ofp8.dequantize_vt(V8, vs, w.l), scale, w.rank, w.N,
+                                     ref[sel], chk)
+        err = np.abs(got - ref)
+        worst = max(worst, float((err[sel] / bO).max()))
+        max_err, max_ref = max(max_err, float(err.max())), max(max_ref, float(np.abs(ref).max()))
+    return ({"value": round(flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+             "kind": "oracle",
+             "sample": f"{n} random query rows of heads {heads} of the same share: oracle "
+                       f"quantization of those heads (untimed), then dequantization and fp64 "
+                       f"attention ({flops:.3e} FLOP, {cpu_s:.1f} s)"},
+            {"rows": n, "max_abs_err": max_err, "max_rel_to_max_ref": max_err / max_ref,
+             "worst_err_over_fp8_bound": worst, "bound_rows": n_bound,
+             "ok": bool(worst <= 1.0)})
 
 
 def causal_sweep(w, args):

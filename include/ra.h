@@ -243,6 +243,57 @@ int ra_causal_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int3
  * 8 * B * H * l_q (two floats per row).  Returns -RA_EINVAL for negative sizes. */
 int64_t ra_share_backward_workspace(int32_t B, int32_t H, int64_t l_q);
 
+/*
+ * FP8 (OCP E4M3) inputs with block quantization (aliyun FlashAttention explainer,
+ * section 2, FlashAttention-3: the forward products run on FP8 matrix units and block
+ * quantization limits the precision lost).  The pages fix neither the format nor the
+ * blocks; this library uses OCP E4M3 (bias 7, largest value 448, no infinities) and:
+ *   descale = max(amax / 448, 2^-126)      per block, fp32, amax = largest |x|
+ *   code    = E4M3(x * (1 / descale))      round to nearest even, fp32 arithmetic
+ * and a code stands for descale * value(code).  T(seg) = ceil(seg / 64).
+ */
+typedef enum ra_fp8_kind {
+    RA_FP8_ROWS = 0, /* Q, K: one scale per 64-row block of each segment; codes keep the
+                        input layout [B, Hx, n_seg*seg, d]; descale [B, Hx, n_seg, T] */
+    RA_FP8_VT = 1    /* V: one scale per channel over all n_seg*seg rows, descale
+                        [B, Hx, d]; codes stored per 64-row tile transposed,
+                        [B, Hx, n_seg, T, d, 64], columns past a segment's end zero */
+} ra_fp8_kind;
+
+/* T(seg) = ceil(seg / 64); -RA_EINVAL for seg < 0.  Host only. */
+int64_t ra_fp8_tiles(int64_t seg);
+
+/*
+ * Quantizes x (bf16 [B, Hx, n_seg*seg, d], device) to E4M3 codes and descales as above.
+ * For a share, Q is one segment of l rows (n_seg = 1) and K, V are N segments of l rows
+ * (the ring members' blocks).  Pointers: device, 16-byte aligned, caller-owned; the
+ * call writes `codes` and `descale` only (RA_FP8_VT uses descale as scratch for the
+ * maxima before finalising it in place).  seg == 0 is a no-op.  Errors: RA_EINVAL for
+ * a bad kind, B, Hx, n_seg, seg, d (64 or 128) or pointer; RA_ENOTSUP for grids beyond
+ * 2^31 - 1 work-groups or a device other than gfx950.
+ */
+int ra_quantize_fp8(int32_t kind, int32_t B, int32_t Hx, int32_t n_seg, int64_t seg, int32_t d,
+                    const void *x, void *codes, float *descale, void *stream);
+
+/*
+ * Rank `rank`'s non-causal share (as ra_share_forward) from FP8 inputs, products on the
+ * gfx950 FP8 matrix path, fp32 statistics:
+ *   Q8 [B, H, l, d] codes with q_descale [B, H, T(l)]          (RA_FP8_ROWS, n_seg = 1)
+ *   K8 [B, H_kv, L, d] codes with k_descale [B, H_kv, N, T(l)] (RA_FP8_ROWS, n_seg = N)
+ *   V8t [B, H_kv, N, T(l), d, 64] codes with v_descale [B, H_kv, d]   (RA_FP8_VT)
+ * computes O = softmax(scale * Qd Kd^T) Vd over the dequantized values, with the
+ * probabilities themselves rounded to E4M3 before they weight V (and the row sum summing
+ * those rounded probabilities).  O fp32 [B, H, l, d]; m_out, l_out as in
+ * ra_share_forward (nullable); O_cast nullable bf16 [B, H, l, d].  Descales must be
+ * positive and finite.  Errors as ra_share_forward; RA_ENOTSUP also when one K head
+ * (L*d bytes) or V head (N*T(l)*64*d bytes) reaches 2^31 bytes.
+ */
+int ra_share_forward_fp8(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                         int32_t d, int32_t B, const void *Q8, const float *q_descale,
+                         const void *K8, const float *k_descale, const void *V8t,
+                         const float *v_descale, float scale, float *O, float *m_out,
+                         float *l_out, void *O_cast, void *stream);
+
 /* Static description of a status code. */
 const char *ra_strerror(int status);
 

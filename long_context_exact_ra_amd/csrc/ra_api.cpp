@@ -352,6 +352,82 @@ int ra_causal_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int3
                            scale, dQ, dK, dV, workspace, stream);
 }
 
+int64_t ra_fp8_tiles(int64_t seg) {
+    if (seg < 0) return -RA_EINVAL;
+    return (seg + 63) / 64;
+}
+
+int ra_quantize_fp8(int32_t kind, int32_t B, int32_t Hx, int32_t n_seg, int64_t seg, int32_t d,
+                    const void *x, void *codes, float *descale, void *stream) {
+    if ((kind != RA_FP8_ROWS && kind != RA_FP8_VT) || B < 1 || Hx < 1 || n_seg < 1 ||
+        seg < 0 || (d != 64 && d != 128))
+        return RA_EINVAL;
+    if (seg == 0) return RA_OK;
+    if (!ptr_ok(x) || !ptr_ok(codes) || !ptr_ok(descale)) return RA_EINVAL;
+    const int64_t heads = (int64_t)B * Hx;
+    const int64_t T = (seg + 63) / 64;
+    const int64_t rows = (int64_t)n_seg * seg;
+    if (heads * n_seg * T > INT32_MAX || heads * ((rows + 255) / 256) > INT32_MAX ||
+        heads * d > INT32_MAX)
+        return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e =
+        kind == RA_FP8_ROWS
+            ? ra::launch_quant_rows(x, (uint8_t *)codes, descale, heads, n_seg, seg, d, st)
+            : ra::launch_quant_vt(x, (uint8_t *)codes, descale, heads, n_seg, seg, d, st);
+    return after_launch(e, st);
+}
+
+int ra_share_forward_fp8(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                         int32_t d, int32_t B, const void *Q8, const float *q_descale,
+                         const void *K8, const float *k_descale, const void *V8t,
+                         const float *v_descale, float scale, float *O, float *m_out,
+                         float *l_out, void *O_cast, void *stream) {
+    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
+        !heads_ok(B, H, H_kv, d, RA_BF16) || !scale_ok(scale))
+        return RA_EINVAL;
+    if (L == 0) return RA_OK;
+    if (!ptr_ok(Q8) || !ptr_ok(q_descale) || !ptr_ok(K8) || !ptr_ok(k_descale) ||
+        !ptr_ok(V8t) || !ptr_ok(v_descale) || !ptr_ok(O) || !opt_ptr_ok(m_out) ||
+        !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast))
+        return RA_EINVAL;
+    const int64_t l = L / N;
+    const int64_t T = (l + 63) / 64;
+    // one K head and one V head are each addressed through a 32-bit byte range
+    if (L * d > INT32_MAX || (int64_t)N * T * 64 * d > INT32_MAX ||
+        (int64_t)N * T * 4 > INT32_MAX)
+        return RA_ENOTSUP;
+    const int64_t qt = (l + ra::fp8_query_tile() - 1) / ra::fp8_query_tile();
+    if (qt * B * H > INT32_MAX) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    ra::Fp8Args a{};
+    a.Q8 = (const uint8_t *)Q8;
+    a.qs = q_descale;
+    a.K8 = (const uint8_t *)K8;
+    a.ks = k_descale;
+    a.V8 = (const uint8_t *)V8t;
+    a.vs = v_descale;
+    a.O = O;
+    a.m = m_out;
+    a.l = l_out;
+    a.O_cast = O_cast;
+    a.l_q = l;
+    a.n_blocks = N;
+    a.rank = rank;
+    a.H = H;
+    a.H_kv = H_kv;
+    a.group = H / H_kv;
+    a.n_tiles_blk = (int32_t)T;
+    a.n_qtiles = (int32_t)qt;
+    a.n_wg = (int32_t)(qt * B * H);
+    a.scale = scale;
+    hipStream_t st = (hipStream_t)stream;
+    return after_launch(ra::launch_fwd_fp8(a, d, st), st);
+}
+
 const char *ra_strerror(int status) {
     switch (status) {
     case RA_OK: return "success";

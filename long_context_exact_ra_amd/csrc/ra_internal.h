@@ -90,6 +90,43 @@ int bwd_key_tile();
 hipError_t launch_bwd_bf16(const BwdArgs &a, const float *O, const void *dO, const float *m,
                            const float *l, int64_t rows, int d, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs &a, int B, int d, int mode, hipStream_t st);
+
+// FP8 (OCP e4m3) share: one launch over every (batch, head, query tile), non-causal.
+// Byte layouts (T = ceil(l / 64) tiles per member block of l rows):
+//   Q8 [B, H, l, D], q_descale [B, H, T]; K8 [B, H_kv, N*l, D], k_descale [B, H_kv, N, T];
+//   V8 [B, H_kv, N, T, D, 64] (each 64-key tile stored transposed), v_descale [B, H_kv, D].
+struct Fp8Args {
+    const uint8_t *Q8;
+    const float *qs;
+    const uint8_t *K8;
+    const float *ks;
+    const uint8_t *V8;
+    const float *vs;
+    float *O;      // [B, H, l, D] finalised output
+    float *m;      // nullable
+    float *l;      // nullable
+    void *O_cast;  // nullable, bf16 [B, H, l, D]
+    int64_t l_q;   // rows per member block (= l)
+    int32_t n_blocks;
+    int32_t rank;
+    int32_t H;
+    int32_t H_kv;
+    int32_t group;
+    int32_t n_tiles_blk;  // T
+    int32_t n_qtiles;
+    int32_t n_wg;
+    float scale;
+};
+int fp8_query_tile();
+hipError_t launch_fwd_fp8(const Fp8Args &a, int d, hipStream_t st);
+
+// FP8 quantization (see ra_quantize_fp8): rows mode writes codes in the input layout and
+// one descale per 64-row block of each segment; vt mode writes per-channel descales over
+// all rows and tile-transposed codes.
+hipError_t launch_quant_rows(const void *x, uint8_t *codes, float *descale, int64_t heads,
+                             int32_t n_seg, int64_t seg, int d, hipStream_t st);
+hipError_t launch_quant_vt(const void *x, uint8_t *codes, float *descale, int64_t heads,
+                           int32_t n_seg, int64_t seg, int d, hipStream_t st);
 hipError_t launch_state_init(float *O_acc, float *m, float *l, int64_t rows, int d,
                              hipStream_t st);
 hipError_t launch_finalize(float *O_acc, const float *l, int64_t rows, int d, int dtype,

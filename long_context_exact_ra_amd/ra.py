@@ -17,6 +17,7 @@ import torch
 RA_OK, RA_EINVAL, RA_ENOTSUP, RA_EHIP = 0, 1, 2, 3
 RA_F32, RA_BF16 = 0, 1
 RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
+RA_FP8_ROWS, RA_FP8_VT = 0, 1
 LAYOUTS = {"contiguous": RA_LAYOUT_CONTIGUOUS, "striped": RA_LAYOUT_STRIPED,
            "zigzag": RA_LAYOUT_ZIGZAG}
 
@@ -75,6 +76,10 @@ def load():
                                                     i32, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                                     vp, vp, vp, vp]),
         "ra_share_backward_workspace": (i64, [i32, i32, i64]),
+        "ra_fp8_tiles": (i64, [i64]),
+        "ra_quantize_fp8": (ctypes.c_int, [i32, i32, i32, i32, i64, i32, vp, vp, vp, vp]),
+        "ra_share_forward_fp8": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, vp, vp, vp,
+                                                vp, vp, vp, f32, vp, vp, vp, vp, vp]),
         "ra_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "ra_last_hip_error": (ctypes.c_int, []),
     }
@@ -90,7 +95,7 @@ def exported_symbols() -> list[str]:
     return ["ra_ring_block", "ra_ring_schedule", "ra_kv_head", "ra_state_init", "ra_step",
             "ra_finalize", "ra_share_forward", "ra_causal_share_forward", "ra_causal_pairs",
             "ra_share_backward", "ra_causal_share_backward", "ra_share_backward_workspace",
-            "ra_strerror",
+            "ra_fp8_tiles", "ra_quantize_fp8", "ra_share_forward_fp8", "ra_strerror",
             "ra_last_hip_error"]
 
 
@@ -326,3 +331,63 @@ def causal_share_backward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, 
     in ra.h); arguments as in share_backward."""
     _backward(rank, N, L, H, H_kv, d, B, layout, Q_i, K, V, O, dO, m, l, scale, dQ, dK, dV,
               workspace, stream)
+
+
+# ------------------------------------------------------------------ FP8
+
+def fp8_tiles(seg: int) -> int:
+    """ceil(seg / 64): scale blocks per segment / stored V tiles per member block."""
+    n = int(load().ra_fp8_tiles(seg))
+    if n < 0:
+        raise RaError(-n, "ra_fp8_tiles")
+    return n
+
+
+def quantize_fp8(kind, x, n_seg: int, codes, descale, stream=None):
+    """Block quantization of bf16 x [B, Hx, n_seg*seg, d] to E4M3 (see ra_quantize_fp8 in
+    ra.h).  kind "rows" (Q, K): codes uint8 like x, descale [B, Hx, n_seg, T]; kind "vt"
+    (V): codes uint8 [B, Hx, n_seg, T, d, 64], descale [B, Hx, d]."""
+    k = {"rows": RA_FP8_ROWS, "vt": RA_FP8_VT}.get(kind, kind)
+    B, Hx, R, d = x.shape
+    if n_seg < 1 or R % n_seg != 0:
+        raise ValueError("rows must split evenly into n_seg segments")
+    seg = R // n_seg
+    T = fp8_tiles(seg)
+    _need_shape(x, (B, Hx, R, d), "x", torch.bfloat16)
+    if k == RA_FP8_ROWS:
+        _need_shape(codes, (B, Hx, R, d), "codes", torch.uint8)
+        _need_shape(descale, (B, Hx, n_seg, T), "descale", torch.float32)
+    else:
+        _need_shape(codes, (B, Hx, n_seg, T, d, 64), "codes", torch.uint8)
+        _need_shape(descale, (B, Hx, d), "descale", torch.float32)
+    _check(load().ra_quantize_fp8(int(k), B, Hx, n_seg, seg, d, _dev(x, "x"),
+                                  _dev(codes, "codes"), _dev(descale, "descale"),
+                                  _stream(stream)), "ra_quantize_fp8")
+
+
+def share_forward_fp8(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int, Q8, qs, K8,
+                      ks, V8t, vs, scale: float, O, m_out=None, l_out=None, O_cast=None,
+                      stream=None):
+    """Rank `rank`'s share from E4M3 inputs (see ra_share_forward_fp8 in ra.h)."""
+    if N < 1 or L % N != 0:
+        raise ValueError("L must be a multiple of N >= 1")
+    l = L // N
+    T = fp8_tiles(l)
+    _need_shape(Q8, (B, H, l, d), "Q8", torch.uint8)
+    _need_shape(qs, (B, H, 1, T), "q_descale", torch.float32)
+    _need_shape(K8, (B, H_kv, L, d), "K8", torch.uint8)
+    _need_shape(ks, (B, H_kv, N, T), "k_descale", torch.float32)
+    _need_shape(V8t, (B, H_kv, N, T, d, 64), "V8t", torch.uint8)
+    _need_shape(vs, (B, H_kv, d), "v_descale", torch.float32)
+    _need_shape(O, (B, H, l, d), "O", torch.float32)
+    if m_out is not None:
+        _need_shape(m_out, (B, H, l), "m_out", torch.float32)
+    if l_out is not None:
+        _need_shape(l_out, (B, H, l), "l_out", torch.float32)
+    if O_cast is not None:
+        _need_shape(O_cast, (B, H, l, d), "O_cast", torch.bfloat16)
+    _check(load().ra_share_forward_fp8(
+        rank, N, L, H, H_kv, d, B, _dev(Q8, "Q8"), _dev(qs, "q_descale"), _dev(K8, "K8"),
+        _dev(ks, "k_descale"), _dev(V8t, "V8t"), _dev(vs, "v_descale"), float(scale),
+        _dev(O, "O"), _dev(m_out, "m_out"), _dev(l_out, "l_out"), _dev(O_cast, "O_cast"),
+        _stream(stream)), "ra_share_forward_fp8")

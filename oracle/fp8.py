@@ -163,3 +163,48 @@ def share_fp8(Q8, q_descale, K8, k_descale, V8t, v_descale, scale, rank: int, N:
     Kd = dequantize_rows(K8, k_descale, l)
     Vd = dequantize_vt(V8t, v_descale, l)
     return share(Qd, Kd, Vd, scale, rank, N, rows=rows, nthreads=nthreads)
+
+
+def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows):
+    """Allowed deviation of an FP8 share from the exact share over the dequantized values
+    Qd, Kd, Vd (fp64), for the listed flat rows (O_ref: the exact rows).  Returns
+    (bound_O [n, d], bound_m [n], bound_l [n]).
+
+    The rounding steps it allows for, beyond the dequantized inputs themselves:
+    * the FP8 matrix instruction's grouped accumulation: each group of 8 consecutive
+      products is summed with its terms truncated to 13 fractional bits below the
+      group's largest product (measured on gfx950), so a score is off by at most
+      ds_k = 2^-10 * scale * sum_d |q_d k_d|, and the P V and row-sum products by 2^-10 of
+      their magnitude sums;
+    * E4M3 rounding of each probability, taken relative to a reference at least 2^4 below
+      the row maximum: relative 2^-4 for P_k >= 2^-10 (row maximum 1), absolute 2^-14
+      below;
+    * fp32 accumulation over L keys (L * 2^-23 relative to the magnitude sum).
+    With e_k = max(2^-4 P_k, 2^-14) + 1.1 P_k expm1(ds_k):
+      |O - O_ref| <= 2 sum_k e_k |V_k - O_ref| / Z + (2^-9 + L 2^-23) sum_k P_k |V_k| / Z + 1e-6
+      |m - M|     <= max_k ds_k + 1e-6 max(1, |M|)
+      |l - Z|     <= 2 sum_k e_k + sum_k P_k expm1(ds_k + max_k ds_k) + (2^-9 + L 2^-23) Z
+    (the factor 2 covers the row sum's own deviation in the denominator)."""
+    from . import ring_schedule
+    B, H, l, d = Qd.shape
+    H_kv, L = Kd.shape[1], Kd.shape[2]
+    g = H // H_kv
+    keys = np.concatenate([np.arange(j * l, (j + 1) * l) for j in ring_schedule(rank, N)])
+    acc = 2.0 ** -9 + L * 2.0 ** -23
+    rows = np.asarray(rows, dtype=np.int64)
+    bO = np.empty((len(rows), d))
+    bm = np.empty(len(rows))
+    bl = np.empty(len(rows))
+    for i, r in enumerate(rows):
+        b, h, q = r // (H * l), (r // l) % H, r % l
+        k, v = Kd[b, h // g][keys], Vd[b, h // g][keys]
+        s = scale * (k @ Qd[b, h, q])
+        ds = 2.0 ** -10 * scale * (np.abs(k) @ np.abs(Qd[b, h, q]))
+        P = np.exp(s - s.max())
+        Z = P.sum()
+        e = np.maximum(2.0 ** -4 * P, 2.0 ** -14) + 1.1 * P * np.expm1(ds)
+        bO[i] = (2 * (e @ np.abs(v - O_ref[i])) + acc * (P @ np.abs(v))) / Z + 1e-6
+        bm[i] = ds.max() + 1e-6 * max(1.0, abs(s.max()))
+        bl[i] = 2 * e.sum() + P @ np.expm1(ds + ds.max()) + acc * Z
+    return bO, bm, bl
+

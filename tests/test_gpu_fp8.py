@@ -1,0 +1,229 @@
+"""GPU parity of the FP8 path: ra_quantize_fp8 (bit-exact against the oracle's
+quantizer) and ra_share_forward_fp8 (against the fp64 share over the dequantized inputs).
+
+Tolerance of the FP8 share (derived; the pages give none): oracle.fp8.error_bounds.  Two
+roundings separate the kernel from exact arithmetic on the dequantized inputs: the FP8
+matrix instruction sums each group of 8 consecutive products with the terms truncated to
+13 fractional bits below the group's largest product (measured on the GPU by an
+in-bounds probe: 2^4 + 2^-9 is kept, 2^5 + 2^-9 loses the 2^-9, terms 8 apart are summed
+exactly), which moves a score by at most 2^-10 * scale * sum_d |q_d k_d|; and each
+probability is rounded to E4M3 (relative 2^-4, or 2^-14 absolute below 2^-10 of the row
+maximum, since the kernel's exponent reference sits at least 2^4 below the maximum).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8 as ofp8
+from long_context_exact_ra_amd import ra, synth
+from test_gpu_parity import _say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    ra.load()
+    return torch.device("cuda:0")
+
+
+def _bits(t):
+    return synth.to_oracle_array(t)
+
+
+def quantize_gpu(x, kind, n_seg, dev):
+    B, Hx, R, d = x.shape
+    seg = R // n_seg
+    T = ra.fp8_tiles(seg)
+    xd = x.to(dev)
+    if kind == "rows":
+        codes = torch.full((B, Hx, R, d), 0xAB, dtype=torch.uint8, device=dev)
+        ds = torch.full((B, Hx, n_seg, T), float("nan"), dtype=torch.float32, device=dev)
+    else:
+        codes = torch.full((B, Hx, n_seg, T, d, 64), 0xAB, dtype=torch.uint8, device=dev)
+        ds = torch.full((B, Hx, d), float("nan"), dtype=torch.float32, device=dev)
+    ra.quantize_fp8(kind, xd, n_seg, codes, ds)
+    torch.cuda.synchronize()
+    return codes, ds
+
+
+def quantize_both(x, kind, n_seg, dev):
+    """GPU and oracle quantization of the same bf16 tensor; asserts bit equality."""
+    codes, ds = quantize_gpu(x, kind, n_seg, dev)
+    seg = x.shape[2] // n_seg
+    fn = ofp8.quantize_rows if kind == "rows" else ofp8.quantize_vt
+    rc, rds = fn(_bits(x), n_seg, seg)
+    gc, gds = codes.cpu().numpy(), ds.cpu().numpy()
+    assert gds.shape == rds.shape and gc.shape == rc.shape
+    assert np.array_equal(gds.view(np.uint32), rds.view(np.uint32)), f"{kind} descale bits"
+    bad = np.count_nonzero(gc != rc)
+    assert bad == 0, f"{kind}: {bad} of {gc.size} codes differ"
+    return codes, ds, rc, rds
+
+
+# (B, Hx, n_seg, seg, d): ragged segments, one-row segments, both head sizes
+QUANT_CASES = [
+    (1, 2, 1, 256, 128),
+    (2, 3, 3, 100, 64),
+    (1, 1, 4, 1, 128),
+    (1, 2, 2, 4096, 128),
+    (1, 4, 8, 70, 64),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("kind", ["rows", "vt"])
+def test_quantize_bit_exact(dev, case, kind):
+    B, Hx, n_seg, seg, d = case
+    g = torch.Generator().manual_seed(700 + seg + d)
+    x = torch.randn((B, Hx, n_seg * seg, d), generator=g)
+    x = x * torch.exp2(torch.randint(-8, 8, (B, Hx, n_seg * seg, 1), generator=g).float())
+    x = x.to(torch.bfloat16)
+    quantize_both(x, kind, n_seg, dev)
+
+
+def test_quantize_zero_and_extreme_blocks(dev):
+    x = torch.zeros((1, 2, 192, 64))
+    x[0, 0, 64:128] = 3e38          # near the fp32 limit
+    x[0, 0, 128:] = 1e-38           # tiny normal values
+    x[0, 1, 5, 7] = -2.0 ** -130    # a subnormal in an otherwise zero block
+    x = x.to(torch.bfloat16)
+    for kind in ("rows", "vt"):
+        quantize_both(x, kind, 1, dev)
+
+
+def run_fp8_share(q, k, v, N, rank, scale, dev, cast=False):
+    """GPU quantization of bf16 q, k, v and the FP8 share; returns the outputs and the
+    GPU codes / descales."""
+    B, H, l, d = q.shape
+    H_kv, L = k.shape[1], k.shape[2]
+    Q8, qs = quantize_gpu(q, "rows", 1, dev)
+    K8, ks = quantize_gpu(k, "rows", N, dev)
+    V8, vs = quantize_gpu(v, "vt", N, dev)
+    O = torch.full((B, H, l, d), float("nan"), dtype=torch.float32, device=dev)
+    m = torch.full((B, H, l), float("nan"), dtype=torch.float32, device=dev)
+    lo = torch.full((B, H, l), float("nan"), dtype=torch.float32, device=dev)
+    Oc = torch.empty((B, H, l, d), dtype=torch.bfloat16, device=dev) if cast else None
+    ra.share_forward_fp8(rank, N, L, H, H_kv, d, B, Q8, qs, K8, ks, V8, vs, scale, O, m, lo, Oc)
+    torch.cuda.synchronize()
+    return (O, m, lo, Oc), (Q8, qs, K8, ks, V8, vs)
+
+
+def oracle_codes(q, k, v, N):
+    """The oracle's own quantization of the same bf16 inputs."""
+    l = q.shape[2]
+    rQ8, rqs = ofp8.quantize_rows(_bits(q), 1, l)
+    rK8, rks = ofp8.quantize_rows(_bits(k), N, l)
+    rV8, rvs = ofp8.quantize_vt(_bits(v), N, l)
+    return rQ8, rqs, rK8, rks, rV8, rvs
+
+
+def assert_codes_equal(gpu, ref, tag):
+    for name, g, r in zip(("Q8", "q_descale", "K8", "k_descale", "V8t", "v_descale"), gpu, ref):
+        g = np.ascontiguousarray(g.cpu().numpy() if isinstance(g, torch.Tensor) else g)
+        assert g.shape == r.shape, f"{tag} {name} shape"
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8)), f"{tag}: {name} differs"
+
+
+def compare_rows(O, m, lo, Oc, ref_codes, scale, rank, N, rows, tag, out_rows=None):
+    """O/m/l/cast rows of the GPU output (flat rows `out_rows`, default `rows`) against
+    the oracle share over `ref_codes` at its flat rows `rows`."""
+    rQ8, rqs, rK8, rks, rV8, rvs = ref_codes
+    l, d = rQ8.shape[2], rQ8.shape[3]
+    rows = np.asarray(rows, dtype=np.int64)
+    out_rows = rows if out_rows is None else np.asarray(out_rows, dtype=np.int64)
+    Or, M, Z = ofp8.share_fp8(rQ8, rqs, rK8, rks, rV8, rvs, scale, rank, N, rows=rows)
+    Qd = ofp8.dequantize_rows(rQ8, rqs, l)
+    Kd = ofp8.dequantize_rows(rK8, rks, l)
+    Vd = ofp8.dequantize_vt(rV8, rvs, l)
+    bO, bm, bl = ofp8.error_bounds(Qd, Kd, Vd, scale, rank, N, Or, rows)
+    rt = torch.from_numpy(out_rows).to(O.device)
+    go = O.reshape(-1, d)[rt].double().cpu().numpy()
+    gm = m.reshape(-1)[rt].double().cpu().numpy()
+    gl = lo.reshape(-1)[rt].double().cpu().numpy()
+    err = np.abs(go - Or)
+    assert np.isfinite(go).all()
+    worst = (err / bO).max()
+    assert worst <= 1.0, f"{tag}: O err/bound {worst:.3f}, max abs err {err.max():.3e}"
+    assert np.all(np.abs(gm - M) <= bm), f"{tag}: m err/bound {(np.abs(gm - M) / bm).max():.3f}"
+    assert np.all(np.abs(gl - Z) <= bl), f"{tag}: l err/bound {(np.abs(gl - Z) / bl).max():.3f}"
+    gc = Oc.reshape(-1, d)[rt].cpu()
+    assert torch.equal(gc, torch.from_numpy(go).float().to(torch.bfloat16)), f"{tag}: cast"
+    rel = err.max() / np.abs(Or).max()
+    _say(f"fp8 share {tag}: worst O err/bound {worst:.3f}, max abs err {err.max():.2e} "
+         f"({100 * rel:.2f} % of max |O|); m err/bound {(np.abs(gm - M) / bm).max():.3f}, "
+         f"l err/bound {(np.abs(gl - Z) / bl).max():.3f}")
+    return worst
+
+
+def check_fp8_share(q, k, v, N, rank, scale, dev, tag=""):
+    B, H, l, d = q.shape
+    (O, m, lo, Oc), gpu_codes = run_fp8_share(q, k, v, N, rank, scale, dev, cast=True)
+    ref = oracle_codes(q, k, v, N)
+    assert_codes_equal(gpu_codes, ref, tag)
+    return compare_rows(O, m, lo, Oc, ref, scale, rank, N, np.arange(B * H * l), tag)
+
+
+# (B, H, H_kv, d, N, l): ragged tails, GQA, both head sizes, N = 1
+SHARE_CASES = [
+    (1, 2, 2, 128, 4, 256),
+    (1, 4, 2, 64, 3, 200),
+    (2, 2, 1, 128, 2, 300),
+    (1, 3, 3, 128, 1, 64),
+    (1, 2, 2, 64, 5, 1000),
+    (1, 1, 1, 128, 2, 33),
+]
+
+
+@pytest.mark.parametrize("case", SHARE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fp8_share_against_the_oracle(dev, case):
+    B, H, H_kv, d, N, l = case
+    q, k, v = synth.draw(B, H, H_kv, d, l, N * l, "bf16", 800 + l + N)
+    check_fp8_share(q, k, v, N, N // 2, 1.0 / math.sqrt(d), dev, tag=str(case))
+
+
+def test_fp8_share_large_logits(dev):
+    """Q/K with std 3: peaked rows, many probabilities deep in the E4M3 subnormals."""
+    B, H, H_kv, d, N, l = 1, 2, 2, 128, 4, 512
+    q, k, v = synth.draw(B, H, H_kv, d, l, N * l, "bf16", 901, qk_std=3.0)
+    check_fp8_share(q, k, v, N, 1, 1.0 / math.sqrt(d), dev, tag="std 3")
+
+
+def test_fp8_share_every_rank(dev):
+    """Every member's ring order: the exact share is the same softmax over all keys, while
+    the kernel's exponent reference, and with it the E4M3 rounding of the probabilities,
+    follows the visiting order; each rank must meet the bound on its own."""
+    B, H, H_kv, d, N, l = 1, 2, 1, 128, 4, 256
+    q, k, v = synth.draw(B, H, H_kv, d, l, N * l, "bf16", 902)
+    ref = oracle_codes(q, k, v, N)
+    for r in range(N):
+        (O, m, lo, Oc), gpu = run_fp8_share(q, k, v, N, r, 0.09, dev, cast=True)
+        assert_codes_equal(gpu, ref, f"rank {r}")
+        compare_rows(O, m, lo, Oc, ref, 0.09, r, N, np.arange(B * H * l), f"rank {r}")
+
+
+@pytest.mark.parametrize("name", ["share_L32K_N8", "share_L128K_N8"])
+def test_fp8_full_size_sampled_rows(dev, name):
+    """The bf16 workloads' shapes quantized and run on the GPU in one launch each; for two
+    heads the oracle quantizes the same bf16 inputs itself (codes compared bit for bit)
+    and evaluates sampled rows on both sides of query-tile boundaries."""
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.draw_workload(w)
+    scale = 1.0 / math.sqrt(w.d)
+    _say(f"[fp8 {name}] quantizing and running the share on the GPU")
+    (O, m, lo, Oc), gpu = run_fp8_share(q, k, v, w.N, w.rank, scale, dev, cast=True)
+    Q8, qs, K8, ks, V8, vs = gpu
+    group = w.H // w.H_kv
+    local = np.array([0, 63, 64, 255, 256, 1000, w.l // 2, w.l - 257, w.l - 1], np.int64)
+    for h in (3, w.H - 1):
+        g = h // group
+        _say(f"[fp8 {name}] oracle quantization and {len(local)} rows of head {h}")
+        ref = oracle_codes(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], w.N)
+        assert_codes_equal((Q8[:, h:h + 1], qs[:, h:h + 1], K8[:, g:g + 1], ks[:, g:g + 1],
+                            V8[:, g:g + 1], vs[:, g:g + 1]), ref, f"{name} head {h}")
+        compare_rows(O, m, lo, Oc, ref, scale, w.rank, w.N, local, f"{name} head {h}",
+                     out_rows=h * w.l + local)

@@ -170,3 +170,49 @@ def test_share_fp8_equals_the_plain_share_on_exactly_representable_inputs():
         np.testing.assert_allclose(O8, O, rtol=0, atol=1e-12 * np.abs(O).max())
         np.testing.assert_allclose(M8, M, rtol=1e-15)
         np.testing.assert_allclose(Z8, Z, rtol=1e-12)
+
+
+def test_error_bounds_cover_a_cpu_model_of_the_kernel_roundings():
+    """A numpy model of what the bound allows for (probabilities rounded to E4M3 relative
+    to a reference 2^4 below the row maximum, grouped accumulation truncating terms 13
+    bits below each group's largest) stays inside oracle.fp8.error_bounds, and a planted
+    mistake in the model (a dropped key) does not."""
+    rng = np.random.default_rng(21)
+    B, H, d, N, l = 1, 1, 64, 2, 96
+    L = N * l
+    Q = rng.standard_normal((B, H, l, d)) * 2
+    K = rng.standard_normal((B, H, L, d)) * 2
+    V = rng.standard_normal((B, H, L, d))
+    scale = 1 / 8
+    rows = np.arange(l)
+    O, M, Z = oracle.share(Q.astype(np.float64), K, V, scale, 0, N, rows=rows)
+    bO, bm, bl = fp8.error_bounds(Q, K, V, scale, 0, N, O, rows)
+
+    def trunc_group_sum(terms):  # groups of 8, terms truncated 13 bits below the max
+        out = 0.0
+        for g0 in range(0, len(terms), 8):
+            t = terms[g0:g0 + 8]
+            e = np.floor(np.log2(np.abs(t).max())) if np.any(t) else 0
+            step = 2.0 ** (e - 13)
+            out += np.sum(np.trunc(t / step) * step)
+        return out
+
+    worst = 0.0
+    for r in rows:
+        s = np.array([trunc_group_sum(scale * Q[0, 0, r] * K[0, 0, k]) for k in range(L)])
+        p = np.exp(s - s.max()) * 16  # reference 2^4 below the maximum
+        pq = fp8.e4m3_decode(fp8.e4m3_encode(p.astype(np.float32)))
+        o = (pq @ V[0, 0]) / pq.sum()
+        worst = max(worst, (np.abs(o - O[r]) / bO[r]).max())
+        lq = pq.sum() / 16
+        assert abs(lq - Z[r]) <= bl[r] and abs(s.max() - M[r]) <= bm[r]
+    assert worst <= 1.0
+    # a dropped key (a plausible kernel mistake) is caught for most rows
+    caught = 0
+    for r in rows[:16]:
+        s = scale * (K[0, 0] @ Q[0, 0, r])
+        p = np.exp(s - s.max())
+        p[np.argmax(p)] = 0.0
+        o = (p @ V[0, 0]) / p.sum()
+        caught += (np.abs(o - O[r]) > bO[r]).any()
+    assert caught >= 12
