@@ -30,13 +30,11 @@
 //
 // Causal shares (one K/V block per ring member, token positions from the layout): the
 // dQ kernel walks only the key tiles of each block that some query of its tile may
-// attend to (a prefix of the block) and limits each lane's keys on the partial ones;
-// the dK/dV kernel walks only the query tiles from the first one holding a query at
-// or after its first key (a suffix) and masks each (query, key) pair by a per-lane
-// threshold (one compare more per element than the ragged-tail mask).  Work-groups
-// with the most work are dispatched first.
-#include <type_traits>
-
+// attend to (a prefix of the block); the dK/dV kernel walks only the query tiles from the
+// first one holding a query at or after its first key (a suffix).  Excluded pairs (and
+// rows past a block's end) get score -inf on the few tiles that hold any, by a per-lane
+// limit, so ordinary tiles pay nothing for masking.  Work-groups with the most work are
+// dispatched first.
 #include "causal_map.h"
 #include "ra_internal.h"
 
@@ -297,17 +295,25 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
             const int allow = cmap.allowed(qa, cc.j, cc.tin * KBC);
             keys = allow < keys ? (allow > 0 ? allow : 0) : keys;
         }
-        const int lim = keys - 4 * hf;
         advance(cc);
+        // Excluded keys get score -inf (so P = 0), on the rare tiles that have any: the
+        // empty volatile asm keeps this a branch rather than selects on every tile.
+        if (__builtin_amdgcn_ballot_w64(keys < KBC) != 0) {
+            asm volatile("" ::: "memory");
+            const int lim = keys - 4 * hf;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)  // key 32 k2 + 8 (i/4) + 4 hf + i%4
+                    if (32 * k2 + 8 * (i >> 2) + (i & 3) >= lim) s[k2][i] = -INFINITY;
+        }
         bf16x8 dsp[4];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = 8 * (c4 & 1) + j;
-                const int key = 32 * (c4 >> 1) + 8 * (i >> 2) + (i & 3);  // minus 4 hf
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c4 >> 1][i], c, -lse2));
-                if (key >= lim) p = 0.f;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c4 >> 1][i], c, -lse2));
                 dsp[c4][j] = (bf16)(p * (dp[c4 >> 1][i] - Dr));
             }
         // dQ^T += K^T dS^T: A = K^T (transposed reads, rows = keys of the contraction).
@@ -419,11 +425,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // hold all the queries that see a key of this work-group; fq is the first query that
     // sees this lane's key (positions grow with the local index in every layout).
     const CausalMap cmap{a.layout, a.rank, a.n_kblocks, kblk};
-    int32_t s_min = 0, fq = 0;
+    int32_t s_min = 0, fq = 0, fq_wave = 0;  // fq_wave: the largest fq of the wave
     if constexpr (CAUSAL) {
-        const int32_t last = kblk - 1;
+        const int32_t last = kblk - 1, wlast = u * KBR + wave * 32 + 31;
         s_min = __builtin_amdgcn_readfirstlane(cmap.first_query(cmap.pos(j, u * KBR)) / QBC);
         fq = cmap.first_query(cmap.pos(j, bl < last ? bl : last));
+        fq_wave = __builtin_amdgcn_readfirstlane(
+            cmap.first_query(cmap.pos(j, wlast < last ? wlast : last)));
     }
     const int32_t act_per_head = tiles_per_head - s_min;
     const int32_t n_tiles = act_per_head * a.group;
@@ -487,14 +495,27 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // (causal), so do queries before this lane's first query fq.  Packed in the contraction
     // order of the gradient products (operand c4: queries 16 c4 + 8 (j/4) + 4 hf + j%4 =
     // elements 8 (c4%2) + j of block c4/2).
-    auto softmax = [&](auto mk, int buf, int32_t t, const f32x16 *sc, const f32x16 *dq,
-                       bf16x8 *pp, bf16x8 *dsp) {
-        constexpr int MK = decltype(mk)::value;
+    // Excluded pairs (rows past the end of the block; causal, queries before this lane's
+    // first query fq) get score -inf, so P = 0 and dS = 0.  Only tiles that have any are
+    // touched, behind a wave-uniform branch kept real by an empty volatile asm.
+    auto mask_tile = [&](int32_t t, f32x16 *sc) {
         int32_t hh;
         const int32_t s_idx = tile_of(t, hh);
+        const bool ragged = (int64_t)(s_idx + 1) * QBC > a.l_q;
+        if (!(ragged || (CAUSAL && fq_wave > s_idx * QBC))) return;
+        asm volatile("" ::: "memory");
         const int64_t left = a.l_q - (int64_t)s_idx * QBC;
         const int qlim = (left < QBC ? (int)left : QBC) - 4 * hf;  // valid query rows
-        const int qthr = fq - s_idx * QBC - 4 * hf;                // first seeing query
+        const int qthr = CAUSAL ? fq - s_idx * QBC - 4 * hf : -QBC;  // first seeing query
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int q = 32 * qb + 8 * (i >> 2) + (i & 3);  // query minus 4 hf
+                if (q >= qlim || q < qthr) sc[qb][i] = -INFINITY;
+            }
+    };
+    auto softmax = [&](int buf, const f32x16 *sc, const f32x16 *dq, bf16x8 *pp, bf16x8 *dsp) {
         const f32x2 *w = Wt[buf];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
@@ -509,9 +530,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * j4 + e, i = 8 * (c4 & 1) + j;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c4 >> 1][i], c, -Lq[e]));
-                    if (MK >= 1 && q0 + e >= qlim) p = 0.f;
-                    if (MK == 2 && q0 + e < qthr) p = 0.f;
+                    const float p =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c4 >> 1][i], c, -Lq[e]));
                     pp[c4][j] = (bf16)p;
                     dsp[c4][j] = (bf16)(p * (dq[c4 >> 1][i] - Dq[e]));
                 }
@@ -541,22 +561,32 @@ void bwd_dkdv_kernel(BwdArgs a) {
     if (n_tiles > 1) load(1, 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    f32x16 s[2], dp[2];
-    scores(0, s, dp);
-    int buf = 0;  // buffer of tile t
-    for (int32_t t = 0; t < n_tiles; ++t) {
-        const int nb = buf == 2 ? 0 : buf + 1;    // tile t + 1
-        const int nnb = nb == 2 ? 0 : nb + 1;     // tile t + 2 (held tile t - 1)
+    // Two score sets alternate (unrolled by two), so the products of tile t+1 never
+    // overwrite registers the exponentials of tile t still read: no copies between
+    // iterations.
+    f32x16 sA[2], dA[2], sB[2], dB[2];
+    scores(0, sA, dA);
+    auto iteration = [&](int32_t t, int buf, f32x16 *sc, const f32x16 *dc, f32x16 *sn,
+                         f32x16 *dn) {
+        const int nb = buf == 2 ? 0 : buf + 1;  // tile t + 1
+        const int nnb = nb == 2 ? 0 : nb + 1;   // tile t + 2 (held tile t - 1)
         if (t + 2 < n_tiles) load(t + 2, nnb);
         bf16x8 pp[4], dsp[4];
-        // (Masking only the tiles that need it, behind a branch, spills at d = 128.)
-        softmax(std::integral_constant<int, CAUSAL ? 2 : 1>{}, buf, t, s, dp, pp, dsp);
-        if (t + 1 < n_tiles) scores(nb, s, dp);
+        mask_tile(t, sc);
+        softmax(buf, sc, dc, pp, dsp);
+        if (t + 1 < n_tiles) scores(nb, sn, dn);
         grads(buf, pp, dsp);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // tile t + 2 landed (this wave's part)
         __syncthreads();                     // everyone's part; tile t fully read
-        buf = nb;
+        return nb;
+    };
+    int buf = 0;  // buffer of tile t
+    int32_t t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+        buf = iteration(t, buf, sA, dA, sB, dB);
+        buf = iteration(t + 1, buf, sB, dB, sA, dA);
     }
+    if (t < n_tiles) iteration(t, buf, sA, dA, sB, dB);
 
     if (!kvalid) return;
     // dk[dt][4 i4 + e]: head-dim 32 dt + 8 i4 + 4 hf + e of this lane's key row; the

@@ -185,11 +185,12 @@ def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows):
       |m - M|     <= max_k ds_k + 1e-6 max(1, |M|)
       |l - Z|     <= 2 sum_k e_k + sum_k P_k expm1(ds_k + max_k ds_k) + (2^-9 + L 2^-23) Z
     (the factor 2 covers the row sum's own deviation in the denominator)."""
-    from . import ring_schedule
+    # A whole share covers every key; the ring order does not enter the sums.
     B, H, l, d = Qd.shape
     H_kv, L = Kd.shape[1], Kd.shape[2]
+    if L != N * l or not 0 <= rank < N:
+        raise ValueError("a share covers all N blocks of l keys")
     g = H // H_kv
-    keys = np.concatenate([np.arange(j * l, (j + 1) * l) for j in ring_schedule(rank, N)])
     acc = 2.0 ** -9 + L * 2.0 ** -23
     rows = np.asarray(rows, dtype=np.int64)
     bO = np.empty((len(rows), d))
@@ -197,7 +198,7 @@ def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows):
     bl = np.empty(len(rows))
     for i, r in enumerate(rows):
         b, h, q = r // (H * l), (r // l) % H, r % l
-        k, v = Kd[b, h // g][keys], Vd[b, h // g][keys]
+        k, v = Kd[b, h // g], Vd[b, h // g]
         s = scale * (k @ Qd[b, h, q])
         ds = 2.0 ** -10 * scale * (np.abs(k) @ np.abs(Qd[b, h, q]))
         P = np.exp(s - s.max())
