@@ -251,3 +251,58 @@ def test_backward_limits_and_noop():
     lib = ra.load()
     assert lib.ra_share_backward_workspace(2, 3, 100) == 8 * 2 * 3 * 100
     assert lib.ra_share_backward_workspace(-1, 3, 100) == -ra.RA_EINVAL
+
+
+# ------------------------------------------------------------------ FP8
+
+def test_fp8_tiles():
+    lib = ra.load()
+    assert [lib.ra_fp8_tiles(s) for s in (0, 1, 63, 64, 65, 16384)] == [0, 1, 1, 1, 2, 256]
+    assert lib.ra_fp8_tiles(-1) == -ra.RA_EINVAL
+
+
+def _quant(**kw):
+    args = dict(kind=ra.RA_FP8_ROWS, B=1, Hx=2, n_seg=4, seg=100, d=128, x=P, codes=P2,
+                descale=P, stream=None)
+    args.update(kw)
+    return ra.load().ra_quantize_fp8(args["kind"], args["B"], args["Hx"], args["n_seg"],
+                                     args["seg"], args["d"], args["x"], args["codes"],
+                                     args["descale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kind=2), dict(kind=-1), dict(B=0), dict(Hx=0), dict(n_seg=0), dict(seg=-1),
+    dict(d=96), dict(x=None), dict(codes=None), dict(descale=None), dict(x=MIS),
+    dict(codes=MIS), dict(descale=MIS)])
+def test_quantize_fp8_rejects(kw):
+    assert _quant(**kw) == ra.RA_EINVAL
+
+
+def test_quantize_fp8_empty_is_noop():
+    assert _quant(seg=0, x=None, codes=None, descale=None) == ra.RA_OK
+    assert _quant(kind=ra.RA_FP8_VT, seg=0) == ra.RA_OK
+
+
+def _fp8(**kw):
+    args = dict(rank=3, N=8, L=8 * 128, H=4, H_kv=2, d=128, B=1, Q=P, qs=P2, K=P, ks=P2, V=P,
+                vs=P2, scale=0.088, O=P2, m=None, l=None, cast=None, stream=None)
+    args.update(kw)
+    return ra.load().ra_share_forward_fp8(
+        args["rank"], args["N"], args["L"], args["H"], args["H_kv"], args["d"], args["B"],
+        args["Q"], args["qs"], args["K"], args["ks"], args["V"], args["vs"], args["scale"],
+        args["O"], args["m"], args["l"], args["cast"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(N=0), dict(rank=8), dict(rank=-1), dict(L=8 * 128 + 1), dict(L=-8), dict(H=5),
+    dict(H_kv=0), dict(d=96), dict(B=0), dict(scale=0.0), dict(scale=float("inf")),
+    dict(Q=None), dict(qs=None), dict(K=None), dict(ks=None), dict(V=None), dict(vs=None),
+    dict(O=None), dict(O=MIS), dict(vs=MIS), dict(m=MIS), dict(cast=MIS)])
+def test_share_forward_fp8_rejects(kw):
+    assert _fp8(**kw) == ra.RA_EINVAL
+
+
+def test_share_forward_fp8_limits_and_noop():
+    assert _fp8(L=0, Q=None, K=None, V=None, O=None) == ra.RA_OK
+    # one K head of L*d bytes must stay below 2^31 (32-bit buffer range)
+    assert _fp8(N=8, L=1 << 24, d=128) == ra.RA_ENOTSUP
