@@ -114,8 +114,8 @@ def main():
     scale = 1.0 / math.sqrt(w.d)
     O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
 
-    if args.fp8 and (args.backward or args.causal or args.step_path):
-        raise SystemExit("--fp8 times the non-causal forward share only")
+    if args.fp8 and (args.backward or args.step_path):
+        raise SystemExit("--fp8 times the forward share (optionally --causal) only")
     extra = {}
     if args.fp8:
         T = ra.fp8_tiles(w.l)
@@ -163,7 +163,7 @@ def main():
     def step():
         if args.fp8:
             ra.share_forward_fp8(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, Q8, qs, K8, ks, V8,
-                                 vs, scale, O)
+                                 vs, scale, O, layout=args.causal)
         elif args.backward and args.causal:
             ra.causal_share_backward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, args.causal, qd,
                                      kd, vd, O, dOd, m_f, l_f, scale, dQ, dK, dV, ws)
@@ -279,6 +279,9 @@ def main():
         metric = f"causal ring-share attention TFLOP/s, useful pairs only ({args.causal} layout)"
     if args.fp8:
         metric = "ring-share attention TFLOP/s (fp8 e4m3 products) + % of fp8 MFMA peak"
+        if args.causal:
+            metric = ("causal ring-share attention TFLOP/s, useful pairs only (fp8 e4m3 "
+                      f"products, {args.causal} layout)")
     if args.backward:
         metric = "ring-share attention backward TFLOP/s (bf16; 2.5x forward FLOPs)"
         if args.causal:
@@ -362,12 +365,18 @@ def fp8_cpu_baseline(w, q, k, v, O, scale, args):
         codes[h] = (*ofp8.quantize_rows(qh, 1, w.l), *ofp8.quantize_rows(kh, w.N, w.l),
                     *ofp8.quantize_vt(vh, w.N, w.l))
     threads = oracle.max_threads()
-    # cost model from two probes: fixed (dequantization) + per row (attention)
+    def run_oracle(c, rows):
+        if args.causal:
+            return ofp8.causal_share_fp8(*c, scale, w.rank, w.N, args.causal, rows=rows)
+        return ofp8.share_fp8(*c, scale, w.rank, w.N, rows=rows)
+
+    # cost model from two probes: fixed (dequantization) + per row (attention); probe rows
+    # from the end of the block, which for a causal share see the most keys
     t = time.perf_counter()
-    ofp8.share_fp8(*codes[heads[0]], scale, w.rank, w.N, rows=list(range(threads)))
+    run_oracle(codes[heads[0]], list(range(w.l - threads, w.l)))
     t1 = time.perf_counter() - t
     t = time.perf_counter()
-    ofp8.share_fp8(*codes[heads[0]], scale, w.rank, w.N, rows=list(range(4 * threads)))
+    run_oracle(codes[heads[0]], list(range(w.l - 4 * threads, w.l)))
     t2 = time.perf_counter() - t
     per_row = max((t2 - t1) / (3 * threads), 1e-6)
     fixed = max(t1 - threads * per_row, 0.0)
@@ -378,11 +387,15 @@ def fp8_cpu_baseline(w, q, k, v, O, scale, args):
     refs, picks = [], []
     for h in heads:
         rows = np.sort(g.choice(w.l, size=per_head, replace=False))
-        refs.append(ofp8.share_fp8(*codes[h], scale, w.rank, w.N, rows=rows)[0])
+        refs.append(run_oracle(codes[h], rows)[0])
         picks.append(rows)
     cpu_s = time.perf_counter() - t
     n = sum(len(p) for p in picks)
-    flops = 4.0 * w.L * w.d * n
+    if args.causal:  # useful pairs only, as the GPU figure
+        qpos = oracle.token_positions(args.causal, w.rank, w.N, w.l)
+        flops = float(sum(np.sum(4.0 * w.d * (qpos[p] + 1)) for p in picks))
+    else:
+        flops = 4.0 * w.L * w.d * n
     import torch
     worst, max_err, max_ref, n_bound = 0.0, 0.0, 0.0, 0
     for h, rows, ref in zip(heads, picks, refs):
@@ -394,7 +407,7 @@ def fp8_cpu_baseline(w, q, k, v, O, scale, args):
         bO, _, _ = ofp8.error_bounds(ofp8.dequantize_rows(Q8, qs, w.l),
                                      ofp8.dequantize_rows(K8, ks, w.l),
                                      ofp8.dequantize_vt(V8, vs, w.l), scale, w.rank, w.N,
-                                     ref[sel], chk)
+                                     ref[sel], chk, layout=args.causal)
         err = np.abs(got - ref)
         worst = max(worst, float((err[sel] / bO).max()))
         max_err, max_ref = max(max_err, float(err.max())), max(max_ref, float(np.abs(ref).max()))

@@ -294,6 +294,19 @@ int ra_share_forward_fp8(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t 
                          const float *v_descale, float scale, float *O, float *m_out,
                          float *l_out, void *O_cast, void *stream);
 
+/*
+ * Rank `rank`'s causal share (as ra_causal_share_forward: each query attends to the keys
+ * at or before its position, slowleelab "Ring Attention" page, 4.5 limitation 2; token
+ * positions from `layout`) from FP8 inputs laid out as for ra_share_forward_fp8.  Key
+ * tiles that no query of a work-group may see are skipped.  RA_LAYOUT_ZIGZAG needs l to be
+ * a multiple of 128, else RA_EINVAL.  Other arguments and errors as ra_share_forward_fp8.
+ */
+int ra_causal_share_forward_fp8(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                                int32_t d, int32_t B, int32_t layout, const void *Q8,
+                                const float *q_descale, const void *K8, const float *k_descale,
+                                const void *V8t, const float *v_descale, float scale, float *O,
+                                float *m_out, float *l_out, void *O_cast, void *stream);
+
 /* Static description of a status code. */
 const char *ra_strerror(int status);
 

@@ -25,6 +25,7 @@
 //    probabilities stay clear of the format's subnormal range.
 //  * Each tile's K scale reaches the lanes with a vector buffer load issued a tile ahead
 //    (a scalar load would force waits on every outstanding LDS read).
+#include "causal_map.h"
 #include "ra_internal.h"
 
 namespace ra {
@@ -82,17 +83,23 @@ __device__ __forceinline__ int key_of_row(int r) {
     return 32 * (r >> 5) + 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3);
 }
 
-struct Cursor {  // ring step t, tile tin of block j(t)
-    int32_t t, tin;
-    __device__ __forceinline__ void next(int32_t T) {
-        if (++tin == T) {
+// Ring step t, tile tin of block j(t); act = tiles of that block that are visited (all
+// of them, or for a causal share the prefix some query of the work-group may see).
+struct Cursor {
+    int32_t t, tin, act;
+    template <typename ActOf>
+    __device__ __forceinline__ void next(const ActOf &act_of, int32_t n_blocks) {
+        if (++tin == act) {
             tin = 0;
-            ++t;
+            do {
+                ++t;
+                act = t < n_blocks ? act_of(t) : 0;
+            } while (t < n_blocks && act == 0);
         }
     }
 };
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     constexpr int NKK = D / 64;        // 64-deep contractions over the head dimension
     constexpr int NDT = D / 32;        // 32-wide output tiles over the head dimension
@@ -113,7 +120,9 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     const int hf = lane >> 5, ln = lane & 31;
 
     const int wg = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, a.n_wg));
-    const int qt = __builtin_amdgcn_readfirstlane(wg % a.n_qtiles);
+    // A causal share gives later query tiles more keys: start those first.
+    const int qt = __builtin_amdgcn_readfirstlane(
+        CAUSAL ? a.n_qtiles - 1 - wg % a.n_qtiles : wg % a.n_qtiles);
     const int bh = __builtin_amdgcn_readfirstlane(wg / a.n_qtiles);
     const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
     const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
@@ -257,11 +266,21 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     // Rare paths (a ragged last tile, a raised reference) stay behind real branches: the
     // empty volatile asm keeps the compiler from turning them into selects and multiplies
     // executed on every tile.
+    // Keys past a block's end and, for a causal share, keys after this lane's query get
+    // score -inf (the limit is per lane; the branch is wave-uniform).
+    const CausalMap cmap{a.layout, a.rank, N, (int32_t)l};
     auto mask_scores = [&](Scores &d, const Cursor &cu) {
         const int64_t left = l - (int64_t)cu.tin * BC;
-        if (left >= BC) return;
+        int keys = left < BC ? (int)left : BC;
+        bool partial = keys < BC;
+        if constexpr (CAUSAL) {
+            const int32_t j = ring_block(a.rank, cu.t, N);
+            keys = min(keys, max(cmap.allowed((int32_t)qrow, j, cu.tin * BC), 0));
+            partial = __builtin_amdgcn_ballot_w64(keys < BC) != 0;
+        }
+        if (!partial) return;
         asm volatile("" ::: "memory");
-        const int lim = (int)left - 16 * hf;  // key = 32 kb + 16 hf + i
+        const int lim = keys - 16 * hf;  // key = 32 kb + 16 hf + i
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -316,20 +335,34 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     // the softmax of tile j+1 and the P V products of tile j.  K(t) in Ks[t & 1], V(t)
     // in Vs[t & 1], P(t) in pb[t & 1]; ks_cur is the K scale of tile j+1, ks_nxt that of
     // tile j+2 (loaded during iteration j).
-    const int32_t n_tiles = T * N;
-    Cursor cK{0, 0}, cV{0, 0}, cM{0, 0}, cS{0, 0};
+    // Last valid local query of the work-group (uniform); positions grow with it.
+    const int64_t a_end = (int64_t)(qt + 1) * BR;
+    const int32_t a_max = (int32_t)((l < a_end ? l : a_end) - 1);
+    auto act_of = [&](int32_t t) -> int32_t {
+        if constexpr (!CAUSAL) return T;
+        else return cmap.active_tiles(ring_block(a.rank, t, N), a_max, BC, T);
+    };
+    int32_t n_tiles = T * N;
+    if constexpr (CAUSAL) {
+        n_tiles = 0;
+        for (int32_t t = 0; t < N; ++t) n_tiles += act_of(t);
+    }
+    // The member's own block comes first and its first tile is always visited (every
+    // query sees its own block's first key), so each row's reference is finite from then.
+    const int32_t act0 = act_of(0);
+    Cursor cK{0, 0, act0}, cV{0, 0, act0}, cM{0, 0, act0}, cS{0, 0, act0};
     load_k(cK, Ks[0]);
-    cK.next(T);
+    cK.next(act_of, N);
     load_v(cV, Vs[0]);
-    cV.next(T);
+    cV.next(act_of, N);
     float ks_cur = load_scale(cS);
-    cS.next(T);
+    cS.next(act_of, N);
     float ks_nxt = 1.f;
     if (n_tiles > 1) {
         load_k(cK, Ks[1]);
-        cK.next(T);
+        cK.next(act_of, N);
         ks_nxt = load_scale(cS);
-        cS.next(T);
+        cS.next(act_of, N);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
@@ -339,7 +372,7 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     {
         scores(Ks[0], sx);
         mask_scores(sx, cM);
-        cM.next(T);
+        cM.next(act_of, N);
         const float ct = tile_scale(ks_cur);
         bool changed;
         const float alpha = update_reference(row_max(sx), ct, changed);
@@ -352,9 +385,9 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     __syncthreads();  // every wave is done with K buffer 0
     if (n_tiles > 2) {
         load_k(cK, Ks[0]);
-        cK.next(T);
+        cK.next(act_of, N);
         ks_nxt = load_scale(cS);
-        cS.next(T);
+        cS.next(act_of, N);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
@@ -367,15 +400,15 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
         const bool more = j + 3 < n_tiles;
         if (more) load_k(cK, knext);
         load_v(cV, vnext);
-        cV.next(T);
+        cV.next(act_of, N);
         float ks_new = 1.f;
         if (more) {
-            cK.next(T);
+            cK.next(act_of, N);
             ks_new = load_scale(cS);
-            cS.next(T);
+            cS.next(act_of, N);
         }
         mask_scores(cs, cM);
-        cM.next(T);
+        cM.next(act_of, N);
         const float ct = tile_scale(ks_cur);
         bool changed;
         const float alpha = update_reference(row_max(cs), ct, changed);
@@ -406,9 +439,9 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     auto tail_iteration = [&](Scores &cs, const uint8_t *vcur, uint8_t *vnext, const i32x8 &pcur,
                               i32x8 &pnxt) {
         load_v(cV, vnext);
-        cV.next(T);
+        cV.next(act_of, N);
         mask_scores(cs, cM);
-        cM.next(T);
+        cM.next(act_of, N);
         const float ct = tile_scale(ks_cur);
         bool changed;
         const float alpha = update_reference(row_max(cs), ct, changed);
@@ -476,9 +509,9 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     }
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t launch(const Fp8Args &a, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_fp8_kernel<D>), dim3(a.n_wg), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(a.n_wg), dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 
@@ -487,8 +520,9 @@ hipError_t launch(const Fp8Args &a, hipStream_t st) {
 int fp8_query_tile() { return BR; }
 
 hipError_t launch_fwd_fp8(const Fp8Args &a, int d, hipStream_t st) {
-    if (d == 128) return launch<128>(a, st);
-    if (d == 64) return launch<64>(a, st);
+    const bool causal = a.layout != kNoCausal;
+    if (d == 128) return causal ? launch<128, true>(a, st) : launch<128, false>(a, st);
+    if (d == 64) return causal ? launch<64, true>(a, st) : launch<64, false>(a, st);
     return hipErrorInvalidValue;
 }
 

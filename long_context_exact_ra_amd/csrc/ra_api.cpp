@@ -196,6 +196,56 @@ int backward_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
         ra::launch_bwd_bf16(a, O, dO, m, l, (int64_t)B * H * lq, d, st), st);
 }
 
+// Shared by ra_share_forward_fp8 (layout kNoCausal) and ra_causal_share_forward_fp8.
+int fp8_share_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, int32_t d,
+                     int32_t B, int32_t layout, const void *Q8, const float *q_descale,
+                     const void *K8, const float *k_descale, const void *V8t,
+                     const float *v_descale, float scale, float *O, float *m_out, float *l_out,
+                     void *O_cast, void *stream) {
+    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
+        !heads_ok(B, H, H_kv, d, RA_BF16) || !scale_ok(scale))
+        return RA_EINVAL;
+    if (L == 0) return RA_OK;
+    if (!ptr_ok(Q8) || !ptr_ok(q_descale) || !ptr_ok(K8) || !ptr_ok(k_descale) ||
+        !ptr_ok(V8t) || !ptr_ok(v_descale) || !ptr_ok(O) || !opt_ptr_ok(m_out) ||
+        !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast))
+        return RA_EINVAL;
+    const int64_t l = L / N;
+    const int64_t T = (l + 63) / 64;
+    // one K head and one V head are each addressed through a 32-bit byte range
+    if (L * d > INT32_MAX || (int64_t)N * T * 64 * d > INT32_MAX ||
+        (int64_t)N * T * 4 > INT32_MAX)
+        return RA_ENOTSUP;
+    const int64_t qt = (l + ra::fp8_query_tile() - 1) / ra::fp8_query_tile();
+    if (qt * B * H > INT32_MAX) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    ra::Fp8Args a{};
+    a.Q8 = (const uint8_t *)Q8;
+    a.qs = q_descale;
+    a.K8 = (const uint8_t *)K8;
+    a.ks = k_descale;
+    a.V8 = (const uint8_t *)V8t;
+    a.vs = v_descale;
+    a.O = O;
+    a.m = m_out;
+    a.l = l_out;
+    a.O_cast = O_cast;
+    a.l_q = l;
+    a.n_blocks = N;
+    a.rank = rank;
+    a.H = H;
+    a.H_kv = H_kv;
+    a.group = H / H_kv;
+    a.n_tiles_blk = (int32_t)T;
+    a.n_qtiles = (int32_t)qt;
+    a.n_wg = (int32_t)(qt * B * H);
+    a.scale = scale;
+    a.layout = layout;
+    hipStream_t st = (hipStream_t)stream;
+    return after_launch(ra::launch_fwd_fp8(a, d, st), st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -385,47 +435,22 @@ int ra_share_forward_fp8(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t 
                          const void *K8, const float *k_descale, const void *V8t,
                          const float *v_descale, float scale, float *O, float *m_out,
                          float *l_out, void *O_cast, void *stream) {
-    if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
-        !heads_ok(B, H, H_kv, d, RA_BF16) || !scale_ok(scale))
+    return fp8_share_launch(rank, N, L, H, H_kv, d, B, ra::kNoCausal, Q8, q_descale, K8,
+                            k_descale, V8t, v_descale, scale, O, m_out, l_out, O_cast, stream);
+}
+
+int ra_causal_share_forward_fp8(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                                int32_t d, int32_t B, int32_t layout, const void *Q8,
+                                const float *q_descale, const void *K8, const float *k_descale,
+                                const void *V8t, const float *v_descale, float scale, float *O,
+                                float *m_out, float *l_out, void *O_cast, void *stream) {
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED &&
+        layout != RA_LAYOUT_ZIGZAG)
         return RA_EINVAL;
-    if (L == 0) return RA_OK;
-    if (!ptr_ok(Q8) || !ptr_ok(q_descale) || !ptr_ok(K8) || !ptr_ok(k_descale) ||
-        !ptr_ok(V8t) || !ptr_ok(v_descale) || !ptr_ok(O) || !opt_ptr_ok(m_out) ||
-        !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast))
+    if (layout == RA_LAYOUT_ZIGZAG && N >= 1 && L >= 0 && L % N == 0 && (L / N) % 128 != 0)
         return RA_EINVAL;
-    const int64_t l = L / N;
-    const int64_t T = (l + 63) / 64;
-    // one K head and one V head are each addressed through a 32-bit byte range
-    if (L * d > INT32_MAX || (int64_t)N * T * 64 * d > INT32_MAX ||
-        (int64_t)N * T * 4 > INT32_MAX)
-        return RA_ENOTSUP;
-    const int64_t qt = (l + ra::fp8_query_tile() - 1) / ra::fp8_query_tile();
-    if (qt * B * H > INT32_MAX) return RA_ENOTSUP;
-    int rc = check_device();
-    if (rc != RA_OK) return rc;
-    ra::Fp8Args a{};
-    a.Q8 = (const uint8_t *)Q8;
-    a.qs = q_descale;
-    a.K8 = (const uint8_t *)K8;
-    a.ks = k_descale;
-    a.V8 = (const uint8_t *)V8t;
-    a.vs = v_descale;
-    a.O = O;
-    a.m = m_out;
-    a.l = l_out;
-    a.O_cast = O_cast;
-    a.l_q = l;
-    a.n_blocks = N;
-    a.rank = rank;
-    a.H = H;
-    a.H_kv = H_kv;
-    a.group = H / H_kv;
-    a.n_tiles_blk = (int32_t)T;
-    a.n_qtiles = (int32_t)qt;
-    a.n_wg = (int32_t)(qt * B * H);
-    a.scale = scale;
-    hipStream_t st = (hipStream_t)stream;
-    return after_launch(ra::launch_fwd_fp8(a, d, st), st);
+    return fp8_share_launch(rank, N, L, H, H_kv, d, B, layout, Q8, q_descale, K8, k_descale,
+                            V8t, v_descale, scale, O, m_out, l_out, O_cast, stream);
 }
 
 const char *ra_strerror(int status) {

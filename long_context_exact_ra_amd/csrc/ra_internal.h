@@ -116,6 +116,7 @@ struct Fp8Args {
     int32_t n_qtiles;
     int32_t n_wg;
     float scale;
+    int32_t layout;  // causal token layout (ra_layout), or kNoCausal
 };
 int fp8_query_tile();
 hipError_t launch_fwd_fp8(const Fp8Args &a, int d, hipStream_t st);

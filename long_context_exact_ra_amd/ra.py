@@ -80,6 +80,9 @@ def load():
         "ra_quantize_fp8": (ctypes.c_int, [i32, i32, i32, i32, i64, i32, vp, vp, vp, vp]),
         "ra_share_forward_fp8": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, vp, vp, vp,
                                                 vp, vp, vp, f32, vp, vp, vp, vp, vp]),
+        "ra_causal_share_forward_fp8": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, i32,
+                                                       vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                                       vp, vp]),
         "ra_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "ra_last_hip_error": (ctypes.c_int, []),
     }
@@ -95,7 +98,8 @@ def exported_symbols() -> list[str]:
     return ["ra_ring_block", "ra_ring_schedule", "ra_kv_head", "ra_state_init", "ra_step",
             "ra_finalize", "ra_share_forward", "ra_causal_share_forward", "ra_causal_pairs",
             "ra_share_backward", "ra_causal_share_backward", "ra_share_backward_workspace",
-            "ra_fp8_tiles", "ra_quantize_fp8", "ra_share_forward_fp8", "ra_strerror",
+            "ra_fp8_tiles", "ra_quantize_fp8", "ra_share_forward_fp8",
+            "ra_causal_share_forward_fp8", "ra_strerror",
             "ra_last_hip_error"]
 
 
@@ -367,8 +371,9 @@ def quantize_fp8(kind, x, n_seg: int, codes, descale, stream=None):
 
 def share_forward_fp8(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int, Q8, qs, K8,
                       ks, V8t, vs, scale: float, O, m_out=None, l_out=None, O_cast=None,
-                      stream=None):
-    """Rank `rank`'s share from E4M3 inputs (see ra_share_forward_fp8 in ra.h)."""
+                      stream=None, layout=None):
+    """Rank `rank`'s share from E4M3 inputs (see ra_share_forward_fp8 in ra.h); with
+    `layout`, the causal share of ra_causal_share_forward_fp8."""
     if N < 1 or L % N != 0:
         raise ValueError("L must be a multiple of N >= 1")
     l = L // N
@@ -386,8 +391,13 @@ def share_forward_fp8(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: i
         _need_shape(l_out, (B, H, l), "l_out", torch.float32)
     if O_cast is not None:
         _need_shape(O_cast, (B, H, l, d), "O_cast", torch.bfloat16)
-    _check(load().ra_share_forward_fp8(
-        rank, N, L, H, H_kv, d, B, _dev(Q8, "Q8"), _dev(qs, "q_descale"), _dev(K8, "K8"),
-        _dev(ks, "k_descale"), _dev(V8t, "V8t"), _dev(vs, "v_descale"), float(scale),
-        _dev(O, "O"), _dev(m_out, "m_out"), _dev(l_out, "l_out"), _dev(O_cast, "O_cast"),
-        _stream(stream)), "ra_share_forward_fp8")
+    args = (_dev(Q8, "Q8"), _dev(qs, "q_descale"), _dev(K8, "K8"), _dev(ks, "k_descale"),
+            _dev(V8t, "V8t"), _dev(vs, "v_descale"), float(scale), _dev(O, "O"),
+            _dev(m_out, "m_out"), _dev(l_out, "l_out"), _dev(O_cast, "O_cast"), _stream(stream))
+    if layout is None:
+        _check(load().ra_share_forward_fp8(rank, N, L, H, H_kv, d, B, *args),
+               "ra_share_forward_fp8")
+    else:
+        _check(load().ra_causal_share_forward_fp8(rank, N, L, H, H_kv, d, B,
+                                                  _layout_code(layout), *args),
+               "ra_causal_share_forward_fp8")

@@ -165,7 +165,19 @@ def share_fp8(Q8, q_descale, K8, k_descale, V8t, v_descale, scale, rank: int, N:
     return share(Qd, Kd, Vd, scale, rank, N, rows=rows, nthreads=nthreads)
 
 
-def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows):
+def causal_share_fp8(Q8, q_descale, K8, k_descale, V8t, v_descale, scale, rank: int, N: int,
+                     layout: str, rows=None, nthreads=None):
+    """The causal share (causal_share: keys at or before each query's position under
+    `layout`) over the dequantized FP8 inputs of share_fp8."""
+    from . import causal_share
+    l = Q8.shape[2]
+    Qd = dequantize_rows(Q8, q_descale, l)
+    Kd = dequantize_rows(K8, k_descale, l)
+    Vd = dequantize_vt(V8t, v_descale, l)
+    return causal_share(Qd, Kd, Vd, scale, rank, N, layout, rows=rows, nthreads=nthreads)
+
+
+def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows, layout=None):
     """Allowed deviation of an FP8 share from the exact share over the dequantized values
     Qd, Kd, Vd (fp64), for the listed flat rows (O_ref: the exact rows).  Returns
     (bound_O [n, d], bound_m [n], bound_l [n]).
@@ -184,7 +196,8 @@ def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows):
       |O - O_ref| <= 2 sum_k e_k |V_k - O_ref| / Z + (2^-9 + L 2^-23) sum_k P_k |V_k| / Z + 1e-6
       |m - M|     <= max_k ds_k + 1e-6 max(1, |M|)
       |l - Z|     <= 2 sum_k e_k + sum_k P_k expm1(ds_k + max_k ds_k) + (2^-9 + L 2^-23) Z
-    (the factor 2 covers the row sum's own deviation in the denominator)."""
+    (the factor 2 covers the row sum's own deviation in the denominator).  With `layout`,
+    the sums run over each row's admissible keys only (the causal share)."""
     # A whole share covers every key; the ring order does not enter the sums.
     B, H, l, d = Qd.shape
     H_kv, L = Kd.shape[1], Kd.shape[2]
@@ -192,6 +205,10 @@ def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows):
         raise ValueError("a share covers all N blocks of l keys")
     g = H // H_kv
     acc = 2.0 ** -9 + L * 2.0 ** -23
+    if layout is not None:
+        from . import layout_positions, token_positions
+        kpos = layout_positions(layout, N, L)
+        qpos = token_positions(layout, rank, N, l)
     rows = np.asarray(rows, dtype=np.int64)
     bO = np.empty((len(rows), d))
     bm = np.empty(len(rows))
@@ -199,6 +216,9 @@ def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows):
     for i, r in enumerate(rows):
         b, h, q = r // (H * l), (r // l) % H, r % l
         k, v = Kd[b, h // g], Vd[b, h // g]
+        if layout is not None:
+            keep = kpos <= qpos[q]
+            k, v = k[keep], v[keep]
         s = scale * (k @ Qd[b, h, q])
         ds = 2.0 ** -10 * scale * (np.abs(k) @ np.abs(Qd[b, h, q]))
         P = np.exp(s - s.max())

@@ -306,3 +306,25 @@ def test_share_forward_fp8_limits_and_noop():
     assert _fp8(L=0, Q=None, K=None, V=None, O=None) == ra.RA_OK
     # one K head of L*d bytes must stay below 2^31 (32-bit buffer range)
     assert _fp8(N=8, L=1 << 24, d=128) == ra.RA_ENOTSUP
+
+
+def _cfp8(**kw):
+    args = dict(rank=3, N=8, L=8 * 128, H=4, H_kv=2, d=128, B=1, layout=0, Q=P, qs=P2, K=P,
+                ks=P2, V=P, vs=P2, scale=0.088, O=P2, m=None, l=None, cast=None, stream=None)
+    args.update(kw)
+    return ra.load().ra_causal_share_forward_fp8(
+        args["rank"], args["N"], args["L"], args["H"], args["H_kv"], args["d"], args["B"],
+        args["layout"], args["Q"], args["qs"], args["K"], args["ks"], args["V"], args["vs"],
+        args["scale"], args["O"], args["m"], args["l"], args["cast"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(layout=3), dict(layout=-1), dict(layout=2, L=8 * 64), dict(layout=2, L=8 * 192),
+    dict(N=0), dict(rank=8), dict(H=5), dict(d=96), dict(scale=0.0), dict(Q=None),
+    dict(vs=MIS), dict(O=MIS)])
+def test_causal_share_forward_fp8_rejects(kw):
+    assert _cfp8(**kw) == ra.RA_EINVAL
+
+
+def test_causal_share_forward_fp8_noop():
+    assert _cfp8(L=0, Q=None, K=None, V=None, O=None) == ra.RA_OK

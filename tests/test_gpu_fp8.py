@@ -96,7 +96,7 @@ def test_quantize_zero_and_extreme_blocks(dev):
         quantize_both(x, kind, 1, dev)
 
 
-def run_fp8_share(q, k, v, N, rank, scale, dev, cast=False):
+def run_fp8_share(q, k, v, N, rank, scale, dev, cast=False, layout=None):
     """GPU quantization of bf16 q, k, v and the FP8 share; returns the outputs and the
     GPU codes / descales."""
     B, H, l, d = q.shape
@@ -108,7 +108,8 @@ def run_fp8_share(q, k, v, N, rank, scale, dev, cast=False):
     m = torch.full((B, H, l), float("nan"), dtype=torch.float32, device=dev)
     lo = torch.full((B, H, l), float("nan"), dtype=torch.float32, device=dev)
     Oc = torch.empty((B, H, l, d), dtype=torch.bfloat16, device=dev) if cast else None
-    ra.share_forward_fp8(rank, N, L, H, H_kv, d, B, Q8, qs, K8, ks, V8, vs, scale, O, m, lo, Oc)
+    ra.share_forward_fp8(rank, N, L, H, H_kv, d, B, Q8, qs, K8, ks, V8, vs, scale, O, m, lo, Oc,
+                         layout=layout)
     torch.cuda.synchronize()
     return (O, m, lo, Oc), (Q8, qs, K8, ks, V8, vs)
 
@@ -129,18 +130,24 @@ def assert_codes_equal(gpu, ref, tag):
         assert np.array_equal(g.view(np.uint8), r.view(np.uint8)), f"{tag}: {name} differs"
 
 
-def compare_rows(O, m, lo, Oc, ref_codes, scale, rank, N, rows, tag, out_rows=None):
+def compare_rows(O, m, lo, Oc, ref_codes, scale, rank, N, rows, tag, out_rows=None,
+                 layout=None):
     """O/m/l/cast rows of the GPU output (flat rows `out_rows`, default `rows`) against
-    the oracle share over `ref_codes` at its flat rows `rows`."""
+    the oracle share (causal under `layout`, if given) over `ref_codes` at its flat rows
+    `rows`."""
     rQ8, rqs, rK8, rks, rV8, rvs = ref_codes
     l, d = rQ8.shape[2], rQ8.shape[3]
     rows = np.asarray(rows, dtype=np.int64)
     out_rows = rows if out_rows is None else np.asarray(out_rows, dtype=np.int64)
-    Or, M, Z = ofp8.share_fp8(rQ8, rqs, rK8, rks, rV8, rvs, scale, rank, N, rows=rows)
+    if layout is None:
+        Or, M, Z = ofp8.share_fp8(rQ8, rqs, rK8, rks, rV8, rvs, scale, rank, N, rows=rows)
+    else:
+        Or, M, Z = ofp8.causal_share_fp8(rQ8, rqs, rK8, rks, rV8, rvs, scale, rank, N, layout,
+                                         rows=rows)
     Qd = ofp8.dequantize_rows(rQ8, rqs, l)
     Kd = ofp8.dequantize_rows(rK8, rks, l)
     Vd = ofp8.dequantize_vt(rV8, rvs, l)
-    bO, bm, bl = ofp8.error_bounds(Qd, Kd, Vd, scale, rank, N, Or, rows)
+    bO, bm, bl = ofp8.error_bounds(Qd, Kd, Vd, scale, rank, N, Or, rows, layout=layout)
     rt = torch.from_numpy(out_rows).to(O.device)
     go = O.reshape(-1, d)[rt].double().cpu().numpy()
     gm = m.reshape(-1)[rt].double().cpu().numpy()
@@ -229,3 +236,54 @@ def test_fp8_full_size_sampled_rows(dev, name):
                             V8[:, g:g + 1], vs[:, g:g + 1]), ref, f"{name} head {h}")
         compare_rows(O, m, lo, Oc, ref, scale, w.rank, w.N, local, f"{name} head {h}",
                      out_rows=h * w.l + local)
+
+
+# ------------------------------------------------------------------ causal FP8 share
+
+# (layout, B, H, H_kv, d, N, l): ragged blocks (contiguous / striped), GQA, both head sizes
+CAUSAL_CASES = [
+    ("contiguous", 1, 2, 1, 128, 3, 300),
+    ("striped", 1, 4, 2, 64, 4, 200),
+    ("zigzag", 1, 2, 2, 128, 4, 256),
+    ("zigzag", 2, 2, 1, 64, 2, 384),
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fp8_causal_share_every_rank(dev, case):
+    layout, B, H, H_kv, d, N, l = case
+    q, k, v = synth.draw(B, H, H_kv, d, l, N * l, "bf16", 950 + l + N)
+    ref = oracle_codes(q, k, v, N)
+    scale = 1.0 / math.sqrt(d)
+    for r in range(N):
+        (O, m, lo, Oc), gpu = run_fp8_share(q, k, v, N, r, scale, dev, cast=True, layout=layout)
+        assert_codes_equal(gpu, ref, f"{case} rank {r}")
+        compare_rows(O, m, lo, Oc, ref, scale, r, N, np.arange(B * H * l),
+                     f"causal {case} rank {r}", layout=layout)
+
+
+def test_fp8_causal_single_member_layouts_agree(dev):
+    """N = 1: every layout is the ordinary causal mask; the three agree bit for bit."""
+    q, k, v = synth.draw(1, 2, 2, 128, 512, 512, "bf16", 960)
+    outs = [run_fp8_share(q, k, v, 1, 0, 0.09, dev, layout=lay)[0][0].cpu()
+            for lay in ("contiguous", "striped", "zigzag")]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+def test_fp8_causal_32k_sampled_rows(dev, layout):
+    w = synth.WORKLOADS["share_L32K_N8"]
+    q, k, v = synth.draw_workload(w)
+    scale = 1.0 / math.sqrt(w.d)
+    _say(f"[fp8 causal 32K {layout}] quantizing and running the share on the GPU")
+    (O, m, lo, Oc), gpu = run_fp8_share(q, k, v, w.N, w.rank, scale, dev, cast=True,
+                                        layout=layout)
+    Q8, qs, K8, ks, V8, vs = gpu
+    local = np.array([0, 63, 64, 255, 256, 2047, 2048, w.l - 1], np.int64)
+    h = w.H - 1
+    ref = oracle_codes(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], w.N)
+    assert_codes_equal((Q8[:, h:h + 1], qs[:, h:h + 1], K8[:, h:h + 1], ks[:, h:h + 1],
+                        V8[:, h:h + 1], vs[:, h:h + 1]), ref, f"32K {layout}")
+    compare_rows(O, m, lo, Oc, ref, scale, w.rank, w.N, local, f"causal 32K {layout}",
+                 out_rows=h * w.l + local, layout=layout)
+

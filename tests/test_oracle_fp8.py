@@ -216,3 +216,30 @@ def test_error_bounds_cover_a_cpu_model_of_the_kernel_roundings():
         o = (p @ V[0, 0]) / p.sum()
         caught += (np.abs(o - O[r]) > bO[r]).any()
     assert caught >= 12
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_causal_share_fp8_equals_the_plain_causal_share_on_exact_inputs(layout):
+    """As for the non-causal share: on exactly representable inputs (every scale 1) the
+    FP8 causal share is the pinned causal share of the plain values."""
+    rng = np.random.default_rng(31)
+    B, H, H_kv, d, N, l = 1, 2, 1, 32, 4, 128
+    grid = fp8.e4m3_decode(np.array([c for c in range(0, 0x7E)], np.uint8))
+
+    def draw(shape):
+        return (rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape)).astype(np.float32)
+
+    Q, K, V = draw((B, H, l, d)), draw((B, H_kv, N * l, d)), draw((B, H_kv, N * l, d))
+    for t in (Q, K):
+        for s0 in range(0, t.shape[2], 64):
+            t[:, :, s0, 0] = 448.0
+    V[:, :, 0, :] = 448.0
+    Q8, qs = fp8.quantize_rows(Q, 1, l)
+    K8, ks = fp8.quantize_rows(K, N, l)
+    V8, vs = fp8.quantize_vt(V, N, l)
+    assert np.all(qs == 1) and np.all(ks == 1) and np.all(vs == 1)
+    for rank in (0, N - 1):
+        O8, M8, Z8 = fp8.causal_share_fp8(Q8, qs, K8, ks, V8, vs, 2.0 ** -15, rank, N, layout)
+        O, M, Z = oracle.causal_share(Q, K, V, 2.0 ** -15, rank, N, layout)
+        np.testing.assert_allclose(O8, O, rtol=0, atol=1e-12 * np.abs(O).max())
+        np.testing.assert_allclose(Z8, Z, rtol=1e-12)
