@@ -44,6 +44,77 @@ def traffic_per_launch(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+class ClockSampler:
+    """Graphics clock (MHz, mean over the XCDs) during the timed steps, from the GPU
+    metrics table that amdsmi (ROCm's Python module) reads.  The table is refreshed by
+    the firmware only every so often, so a reading counts only when the table's
+    accumulated-activity field has moved since the previous one (a fresh table); one
+    more reading is taken right after the steps finish.  mean() is None where the
+    module, the device or the fields are unavailable."""
+
+    def __init__(self, period_s: float = 0.02):
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        self._handle = None
+        self._acc = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self._acc, _ = self._read()
+        except Exception:  # no library, no permission, no device: no clock figure
+            self._handle = None
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = m.get("current_gfxclks")
+        vals = []
+        if isinstance(clks, (list, tuple)):
+            vals = [float(x) for x in clks if isinstance(x, (int, float)) and 0 < x < 10000]
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [float(m["current_gfxclk"])]
+        return m.get("gfx_activity_acc"), (sum(vals) / len(vals) if vals else None)
+
+    def _take(self):
+        acc, clk = self._read()
+        if clk is not None and acc is not None and acc != self._acc:
+            self.samples.append(clk)
+        self._acc = acc
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self._take()
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self._handle is None:
+            return
+        import threading
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        """Call right after the steps have finished (after synchronising)."""
+        if self._thread is None:
+            return
+        self._stop.set()
+        self._thread.join()
+        try:
+            self._take()
+        except Exception:
+            pass
+
+    def mean(self):
+        return sum(self.samples) / len(self.samples) if self.samples else None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -183,13 +254,23 @@ def main():
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    # One event per step boundary as well: the per-step spread beside the mean.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    clock = ClockSampler()
     torch.cuda.synchronize()
+    clock.start()
     t0.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
+    clock.stop()
     ms = t0.elapsed_time(t1) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    extra["step_ms"] = {"median": round(per_step[len(per_step) // 2], 4),
+                        "min": round(per_step[0], 4), "max": round(per_step[-1], 4)}
     print(f"[bench] {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
     flops = w.flops()
     if args.backward:  # S, dP, dV, dK, dQ products: 2.5x the forward's two
@@ -228,6 +309,12 @@ def main():
     peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
+    sclk = clock.mean()
+    # The nominal peak assumes 2.4 GHz; under full matrix load the clock runs lower.
+    extra["sclk"] = {"mean_mhz": round(sclk, 1) if sclk else None,
+                     "samples": len(clock.samples),
+                     "pct_of_peak_at_mean_sclk":
+                         round(100 * tflops / (peak * sclk / 2400.0), 2) if sclk else None}
 
     cpu_baseline = None
     parity = None
