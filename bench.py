@@ -124,8 +124,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
-    p.add_argument("--step-path", action="store_true",
-                   help="also time the per-step path (N x ra_step + ra_finalize)")
+    p.add_argument("--no-step-path", dest="step_path", action="store_false",
+                   help="skip the secondary timing of the per-step path "
+                        "(N x ra_step + ra_finalize), which runs by default")
     p.add_argument("--causal", choices=["contiguous", "striped", "zigzag"], default=None,
                    help="time the causal share under this token layout instead")
     p.add_argument("--rank", type=int, default=None, help="ring member to time")
@@ -185,7 +186,7 @@ def main():
     scale = 1.0 / math.sqrt(w.d)
     O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
 
-    if args.fp8 and (args.backward or args.step_path):
+    if args.fp8 and args.backward:
         raise SystemExit("--fp8 times the forward share (optionally --causal) only")
     extra = {}
     if args.fp8:
@@ -281,7 +282,7 @@ def main():
             flops *= 2.5
     tflops = flops / (ms * 1e-3) / 1e12
 
-    if args.step_path and not args.causal and not args.backward:
+    if args.step_path and not (args.causal or args.backward or args.fp8):
         O_acc = torch.empty_like(O)
         m = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
         s = torch.empty_like(m)

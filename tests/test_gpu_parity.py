@@ -338,3 +338,31 @@ def test_full_size_workload_sampled_rows(dev, name):
                 "bf16", name)
     assert torch.isfinite(O).all()
     _say(f"[{name}] max abs err {err:.2e} over {len(rows)} rows")
+
+
+def test_share_32k_every_row(dev):
+    """The 32K share (4096 query rows of each of 32 heads against 32768 keys) against the
+    oracle on every row, not a sample: O, its bf16 cast and the row statistics.  The
+    oracle runs in chunks of four heads (about 5 s each on 16 host threads)."""
+    w = synth.WORKLOADS["share_L32K_N8"]
+    _say("[32K every row] drawing inputs")
+    q, k, v = synth.draw_workload(w)
+    scale = 1.0 / math.sqrt(w.d)
+    O, m, lo, cast, trace = run_share(q.to(dev), k.to(dev), v.to(dev), w.rank, w.N, scale)
+    assert trace.cpu().tolist() == oracle.ring_schedule(w.rank, w.N)
+    assert torch.isfinite(O).all()
+    Q, K, V = host(q, k, v)
+    Og = O.reshape(-1, w.d).cpu().numpy()
+    cg = cast.reshape(-1, w.d).float().cpu().numpy()
+    mg, lg = m.reshape(-1).cpu().numpy(), lo.reshape(-1).cpu().numpy()
+    n, chunk = w.B * w.H * w.l, 4 * w.l
+    worst = 0.0
+    for r0 in range(0, n, chunk):
+        rows = np.arange(r0, min(n, r0 + chunk), dtype=np.int64)
+        Or, M, Z = oracle.share(Q, K, V, scale, w.rank, w.N, rows=rows)
+        err = check_O(Og[rows], Or, "bf16", f"32K rows {r0}+")
+        check_O(cg[rows], Or, "bf16", f"32K cast rows {r0}+")
+        check_stats(mg[rows], lg[rows], M, Z, "bf16", f"32K rows {r0}+")
+        worst = max(worst, err)
+        _say(f"[32K every row] rows {r0}..{r0 + len(rows) - 1}: max abs err {err:.2e}")
+    _say(f"[32K every row] all {n} rows: max abs err {worst:.2e}")
