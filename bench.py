@@ -398,6 +398,8 @@ def main():
         "cpu_baseline": cpu_baseline,
         "parity": parity,
         "kernel_sha": kernel_sha(),
+        "env": {"torch": torch.__version__, "hip": torch.version.hip,
+                "device": torch.cuda.get_device_name(0)},
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
