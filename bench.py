@@ -155,7 +155,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not "
               "supported (the ring transport across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
