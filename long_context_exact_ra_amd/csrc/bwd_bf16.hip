@@ -35,6 +35,8 @@
 // rows past a block's end) get score -inf on the few tiles that hold any, by a per-lane
 // limit, so ordinary tiles pay nothing for masking.  Work-groups with the most work are
 // dispatched first.
+#include <type_traits>
+
 #include "causal_map.h"
 #include "ra_internal.h"
 
@@ -55,6 +57,20 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
     const int per = n / 8, rem = n % 8;
     const int xcd = wg % 8, slot = wg / 8;
     return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Buffer B of a tile ring held as separate __shared__ arrays.  The compiler separates
+// the direct-to-LDS tile loads into one buffer from the reads of another only when the
+// two are distinct __shared__ objects named at compile time; otherwise it waits for the
+// loads (vmcnt) before every LDS read that follows them.
+template <int B, typename T>
+__device__ __forceinline__ T *pick(T *b0, T *b1, T *b2 = nullptr) {
+    if constexpr (B == 0) return b0;
+    else if constexpr (B == 1) return b1;
+    else return b2;
 }
 
 __device__ __forceinline__ bf16x4 tr_read(const bf16 *p) {
@@ -160,8 +176,12 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NKK = D / 16, NDT = D / 32, TILE = KBC * D;
     using TL = TileLoad<D, KBC, QW>;
-    __shared__ __attribute__((aligned(1024))) bf16 Kt[2][TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 Vt[2][TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Kt0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Kt1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Vt0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Vt1[TILE];
+    auto Kt = [&](auto b) { return pick<decltype(b)::value>(Kt0, Kt1); };
+    auto Vt = [&](auto b) { return pick<decltype(b)::value>(Vt0, Vt1); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -237,11 +257,11 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
         const int32_t left = kblk - cu.tin * KBC;
         return left < KBC ? left : KBC;
     };
-    auto load = [&](const Cursor &cu, int buf) {
+    auto load = [&](const Cursor &cu, auto buf) {
         const int64_t r0 = (int64_t)cu.j * kblk + (int64_t)cu.tin * KBC;
         const uint32_t soff = (uint32_t)(r0 * D * 2);
-        TL::run(krs, soff, tile_rows(cu), Kt[buf], wave, lane);
-        TL::run(vrs, soff, tile_rows(cu), Vt[buf], wave, lane);
+        TL::run(krs, soff, tile_rows(cu), Kt(buf), wave, lane);
+        TL::run(vrs, soff, tile_rows(cu), Vt(buf), wave, lane);
     };
 
     const int rb = row_base<D>(ln, hf);
@@ -253,18 +273,18 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
     advance(lc);
     cc = lc;
     if (n_tiles > 0) {
-        load(lc, 0);
+        load(lc, IC<0>{});
         advance(lc);
     }
-    for (int32_t t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
+    // Tile t in buffer t & 1, fixed at compile time (the loop is unrolled by two).
+    auto step = [&](auto buf, int32_t t) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t landed (this wave's part)
         __syncthreads();                     // ... everyone's part; tile t-1 fully read
         if (t + 1 < n_tiles) {
-            load(lc, buf ^ 1);
+            load(lc, IC<1 - decltype(buf)::value>{});
             advance(lc);
         }
-        const bf16 *kt = Kt[buf], *vt = Vt[buf];
+        const bf16 *kt = Kt(buf), *vt = Vt(buf);
 
         // S^T = K Q^T and dP^T = V dO^T: lane = query ln, 16 keys per 32-key block.
         f32x16 s[2], dp[2];
@@ -326,6 +346,11 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
                 const bf16x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsp[c4], dq[dt], 0, 0, 0);
             }
+    };
+    for (int32_t t = 0; t < n_tiles; t += 2) {
+        step(IC<0>{}, t);
+        if (t + 1 >= n_tiles) break;
+        step(IC<1>{}, t + 1);
     }
 
     if (!qvalid) return;
@@ -377,9 +402,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
     using TL = TileLoad<D, QBC, KW>;
     // Three tile buffers: tile t is read by the gradient products while tile t+1 is read
     // by the score products and tile t+2 is being loaded.
-    __shared__ __attribute__((aligned(1024))) bf16 Qt[3][TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 Ot[3][TILE];  // dO tiles
-    __shared__ __attribute__((aligned(16))) f32x2 Wt[3][QBC];    // (D, lse2) of the rows
+    __shared__ __attribute__((aligned(1024))) bf16 Qt0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Qt1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Qt2[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Ot0[TILE];  // dO tiles
+    __shared__ __attribute__((aligned(1024))) bf16 Ot1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 Ot2[TILE];
+    __shared__ __attribute__((aligned(16))) f32x2 Wt0[QBC];    // (D, lse2) of the rows
+    __shared__ __attribute__((aligned(16))) f32x2 Wt1[QBC];
+    __shared__ __attribute__((aligned(16))) f32x2 Wt2[QBC];
+    auto Qt = [&](auto b) { return pick<decltype(b)::value>(Qt0, Qt1, Qt2); };
+    auto Ot = [&](auto b) { return pick<decltype(b)::value>(Ot0, Ot1, Ot2); };
+    auto Wt = [&](auto b) { return pick<decltype(b)::value>(Wt0, Wt1, Wt2); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -441,7 +475,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         hh = t / act_per_head;
         return s_min + (t - hh * act_per_head);
     };
-    auto load = [&](int32_t t, int buf) {
+    auto load = [&](int32_t t, auto buf) {
         int32_t hh;
         const int32_t s = tile_of(t, hh);
         const int64_t bh = (int64_t)b * a.H + (int64_t)g * a.group + hh;
@@ -453,25 +487,25 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const bf16 *)a.dO + bh * a.l_q * D), 0, head_bytes, kRsrcWord3);
         const uint32_t soff = (uint32_t)(r0 * D * 2);
-        TL::run(qrs, soff, valid, Qt[buf], wave, lane);
-        TL::run(ors, soff, valid, Ot[buf], wave, lane);
+        TL::run(qrs, soff, valid, Qt(buf), wave, lane);
+        TL::run(ors, soff, valid, Ot(buf), wave, lane);
         if (wave == KW - 1 && lane < QBC / 2) {  // 64 (D, lse2) pairs = 512 bytes
             const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)((const f32x2 *)a.ws + bh * a.l_q), 0, (int)(a.l_q * 8), kRsrcWord3);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wrs, (void __attribute__((address_space(3))) *)(&Wt[buf][0]), 16, lane * 16,
+                wrs, (void __attribute__((address_space(3))) *)(Wt(buf)), 16, lane * 16,
                 (int)(r0 * 8), 0, 0);
         }
     };
 
     const int rb = row_base<D>(ln, hf);
-    const int tb_lo = tr_base<D>(lane, 0), tb_hi = tr_base<D>(lane, 1);
+    const int tb_lo0 = tr_base<D>(lane, 0), tb_hi0 = tr_base<D>(lane, 1);
     const float c = a.scale_log2;
 
     // S = Q K^T and dP = dO V^T of the tile in buffer `buf`: lane = key ln, 16 queries per
     // 32-query block, element i of block qb = query 32 qb + 8 (i/4) + 4 hf + i%4.
-    auto scores = [&](int buf, f32x16 *sc, f32x16 *dq) {
-        const bf16 *qt = Qt[buf], *ot = Ot[buf];
+    auto scores = [&](auto buf, f32x16 *sc, f32x16 *dq) {
+        const bf16 *qt = Qt(buf), *ot = Ot(buf);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             sc[qb] = f32x16{};
@@ -515,16 +549,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 if (q >= qlim || q < qthr) sc[qb][i] = -INFINITY;
             }
     };
-    auto softmax = [&](int buf, const f32x16 *sc, const f32x16 *dq, bf16x8 *pp, bf16x8 *dsp) {
-        const f32x2 *w = Wt[buf];
+    auto softmax = [&](auto buf, const f32x16 *sc, const f32x16 *dq, bf16x8 *pp, bf16x8 *dsp) {
+        int wo = 4 * hf;
+        asm volatile("" : "+v"(wo));
+        const f32x2 *w = Wt(buf) + wo;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
             for (int j4 = 0; j4 < 2; ++j4) {
                 // queries q0 .. q0 + 3, q0 = 16 c4 + 8 j4 + 4 hf: two 16-byte LDS reads
                 const int q0 = 16 * c4 + 8 * j4;  // minus 4 hf
-                const f32x4 w01 = *(const f32x4 *)(w + q0 + 4 * hf);
-                const f32x4 w23 = *(const f32x4 *)(w + q0 + 4 * hf + 2);
+                const f32x4 w01 = *(const f32x4 *)(w + q0);
+                const f32x4 w23 = *(const f32x4 *)(w + q0 + 2);
                 const float Dq[4] = {w01[0], w01[2], w23[0], w23[2]};
                 const float Lq[4] = {w01[1], w01[3], w23[1], w23[3]};
 #pragma unroll
@@ -538,8 +574,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
             }
     };
     // dV^T += dO^T P and dK^T += Q^T dS: A = transposed reads of the dO / Q tiles.
-    auto grads = [&](int buf, const bf16x8 *pp, const bf16x8 *dsp) {
-        const bf16 *qt = Qt[buf], *ot = Ot[buf];
+    auto grads = [&](auto buf, const bf16x8 *pp, const bf16x8 *dsp) {
+        const bf16 *qt = Qt(buf), *ot = Ot(buf);
+        int tb_lo = tb_lo0, tb_hi = tb_hi0;  // derived where used, not kept live per buffer
+        asm volatile("" : "+v"(tb_lo), "+v"(tb_hi));
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
@@ -557,19 +595,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
     // Pipeline: iteration t runs the exponentials of tile t beside the score products of
     // tile t+1, then tile t's gradient products; tile t+2 loads meanwhile.
-    load(0, 0);
-    if (n_tiles > 1) load(1, 1);
+    load(0, IC<0>{});
+    if (n_tiles > 1) load(1, IC<1>{});
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // Two score sets alternate (unrolled by two), so the products of tile t+1 never
     // overwrite registers the exponentials of tile t still read: no copies between
     // iterations.
     f32x16 sA[2], dA[2], sB[2], dB[2];
-    scores(0, sA, dA);
-    auto iteration = [&](int32_t t, int buf, f32x16 *sc, const f32x16 *dc, f32x16 *sn,
+    scores(IC<0>{}, sA, dA);
+    // Tile t in buffer t % 3, fixed at compile time (the loop is unrolled by six: three
+    // buffers times two score sets).
+    auto iteration = [&](auto buf, int32_t t, f32x16 *sc, const f32x16 *dc, f32x16 *sn,
                          f32x16 *dn) {
-        const int nb = buf == 2 ? 0 : buf + 1;  // tile t + 1
-        const int nnb = nb == 2 ? 0 : nb + 1;   // tile t + 2 (held tile t - 1)
+        constexpr int b = decltype(buf)::value;
+        const IC<(b + 1) % 3> nb;   // tile t + 1
+        const IC<(b + 2) % 3> nnb;  // tile t + 2 (held tile t - 1)
         if (t + 2 < n_tiles) load(t + 2, nnb);
         bf16x8 pp[4], dsp[4];
         mask_tile(t, sc);
@@ -578,15 +619,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
         grads(buf, pp, dsp);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // tile t + 2 landed (this wave's part)
         __syncthreads();                     // everyone's part; tile t fully read
-        return nb;
     };
-    int buf = 0;  // buffer of tile t
-    int32_t t = 0;
-    for (; t + 1 < n_tiles; t += 2) {
-        buf = iteration(t, buf, sA, dA, sB, dB);
-        buf = iteration(t + 1, buf, sB, dB, sA, dA);
+    for (int32_t t = 0;; t += 6) {
+        iteration(IC<0>{}, t, sA, dA, sB, dB);
+        if (t + 1 >= n_tiles) break;
+        iteration(IC<1>{}, t + 1, sB, dB, sA, dA);
+        if (t + 2 >= n_tiles) break;
+        iteration(IC<2>{}, t + 2, sA, dA, sB, dB);
+        if (t + 3 >= n_tiles) break;
+        iteration(IC<0>{}, t + 3, sB, dB, sA, dA);
+        if (t + 4 >= n_tiles) break;
+        iteration(IC<1>{}, t + 4, sA, dA, sB, dB);
+        if (t + 5 >= n_tiles) break;
+        iteration(IC<2>{}, t + 5, sB, dB, sA, dA);
+        if (t + 6 >= n_tiles) break;
     }
-    if (t < n_tiles) iteration(t, buf, sA, dA, sB, dB);
 
     if (!kvalid) return;
     // dk[dt][4 i4 + e]: head-dim 32 dt + 8 i4 + 4 hf + e of this lane's key row; the

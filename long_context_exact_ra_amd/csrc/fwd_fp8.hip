@@ -112,8 +112,13 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     constexpr int KLD = KTB / 1024, VLD = VTB / 1024;    // 1 KB loads per tile
     static_assert(KTB % 1024 == 0 && VTB % 1024 == 0 && KLD <= 2 * NW && VLD <= 2 * NW, "loads");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t Ks[2][KTB];
-    __shared__ __attribute__((aligned(1024))) uint8_t Vs[2][VTB];
+    // One array per buffer: the compiler tells the tile loads into one buffer apart from
+    // the fragment reads of the other only when they are distinct __shared__ objects, and
+    // otherwise waits for the loads (vmcnt) before every read.
+    __shared__ __attribute__((aligned(1024))) uint8_t Ks0[KTB];
+    __shared__ __attribute__((aligned(1024))) uint8_t Ks1[KTB];
+    __shared__ __attribute__((aligned(1024))) uint8_t Vs0[VTB];
+    __shared__ __attribute__((aligned(1024))) uint8_t Vs1[VTB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -226,12 +231,14 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     };
     // Score product s of a tile (s = 0 .. NDT-1): block kb = s / NKK, contraction kk.
     const int kbase = ln * KROW + 32 * hf;  // row ln, bytes 32 hf .. of each 64-byte step
+    auto k_frag = [&](const uint8_t *kt, int kb0, int s) {
+        const uint8_t *p = kt + kb0 + (s / NKK) * 32 * KROW + 64 * (s % NKK);
+        return join(*(const i32x4 *)p, *(const i32x4 *)(p + 16));
+    };
     auto score_mfma = [&](const uint8_t *kt, int kb0, Scores &d, int s) {
         const int kb = s / NKK, kk = s % NKK;
         if (kk == 0) d.h[kb] = f32x16{};
-        const uint8_t *p = kt + kb0 + kb * 32 * KROW + 64 * kk;
-        const i32x8 kf = join(*(const i32x4 *)p, *(const i32x4 *)(p + 16));
-        d.h[kb] = mfma8(kf, qf[kk], d.h[kb]);
+        d.h[kb] = mfma8(k_frag(kt, kb0, s), qf[kk], d.h[kb]);
     };
     auto laundered = [](int x) {
         asm volatile("" : "+v"(x));  // derive read offsets where used, not kept live
@@ -243,10 +250,12 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
         for (int st = 0; st < NDT; ++st) score_mfma(kt, kb0, d, st);
     };
     const int vbase = ln * VROW + 16 * hf;  // row ln: keys 16 hf .. and 32 + 16 hf ..
-    auto pv_mfma = [&](const uint8_t *vt, int vb, const i32x8 &pb, int dt) {
+    auto v_frag = [&](const uint8_t *vt, int vb, int dt) {
         const uint8_t *p = vt + vb + 32 * VROW * dt;
-        const i32x8 vf = join(*(const i32x4 *)p, *(const i32x4 *)(p + 32));
-        o[dt] = mfma8(vf, pb, o[dt]);
+        return join(*(const i32x4 *)p, *(const i32x4 *)(p + 32));
+    };
+    auto pv_mfma = [&](const uint8_t *vt, int vb, const i32x8 &pb, int dt) {
+        o[dt] = mfma8(v_frag(vt, vb, dt), pb, o[dt]);
     };
     // Kept resident: rebuilt before each use, the eight moves would sit right before
     // the product that reads them and stall it (measured: 12 % of the kernel's time).
@@ -332,9 +341,9 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     auto tile_scale = [&](float ks) { return fmaxf(c_lane * ks, kFltMin); };
 
     // ---- pipeline (as the bf16 kernel): iteration j computes the scores of tile j+2,
-    // the softmax of tile j+1 and the P V products of tile j.  K(t) in Ks[t & 1], V(t)
-    // in Vs[t & 1], P(t) in pb[t & 1]; ks_cur is the K scale of tile j+1, ks_nxt that of
-    // tile j+2 (loaded during iteration j).
+    // the softmax of tile j+1 and the P V products of tile j.  K(t) in Ks0 / Ks1 and V(t)
+    // in Vs0 / Vs1 by the parity of t, P(t) in pb[t & 1]; ks_cur is the K scale of tile
+    // j+1, ks_nxt that of tile j+2 (loaded during iteration j).
     // Last valid local query of the work-group (uniform); positions grow with it.
     const int64_t a_end = (int64_t)(qt + 1) * BR;
     const int32_t a_max = (int32_t)((l < a_end ? l : a_end) - 1);
@@ -351,15 +360,15 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     // query sees its own block's first key), so each row's reference is finite from then.
     const int32_t act0 = act_of(0);
     Cursor cK{0, 0, act0}, cV{0, 0, act0}, cM{0, 0, act0}, cS{0, 0, act0};
-    load_k(cK, Ks[0]);
+    load_k(cK, Ks0);
     cK.next(act_of, N);
-    load_v(cV, Vs[0]);
+    load_v(cV, Vs0);
     cV.next(act_of, N);
     float ks_cur = load_scale(cS);
     cS.next(act_of, N);
     float ks_nxt = 1.f;
     if (n_tiles > 1) {
-        load_k(cK, Ks[1]);
+        load_k(cK, Ks1);
         cK.next(act_of, N);
         ks_nxt = load_scale(cS);
         cS.next(act_of, N);
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
     Scores sx, sy;
     i32x8 pb[2];
     {
-        scores(Ks[0], sx);
+        scores(Ks0, sx);
         mask_scores(sx, cM);
         cM.next(act_of, N);
         const float ct = tile_scale(ks_cur);
@@ -379,12 +388,12 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
         (void)alpha;  // nothing accumulated yet
 #pragma unroll
         for (int q4 = 0; q4 < 8; ++q4) softmax_dw(sx, pb[0], q4, ct);
-        if (n_tiles > 1) scores(Ks[1], sy);
+        if (n_tiles > 1) scores(Ks1, sy);
         ks_cur = ks_nxt;
     }
     __syncthreads();  // every wave is done with K buffer 0
     if (n_tiles > 2) {
-        load_k(cK, Ks[0]);
+        load_k(cK, Ks0);
         cK.next(act_of, N);
         ks_nxt = load_scale(cS);
         cS.next(act_of, N);
@@ -415,10 +424,18 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
         // Stage st: one score product of tile j+2, one P V product of tile j and an
         // equal share of the softmax of tile j+1 (independent work side by side).
         const int kb0 = laundered(kbase), vb = laundered(vbase);
+        // The K and V^T fragments of stage st + 1 are read during stage st.
+        i32x8 kfr = k_frag(kcur, kb0, 0), vfr = v_frag(vcur, vb, 0);
 #pragma unroll
         for (int st = 0; st < NDT; ++st) {
-            score_mfma(kcur, kb0, ns, st);
-            pv_mfma(vcur, vb, pcur, st);
+            i32x8 kn = kfr, vn = vfr;
+            if (st + 1 < NDT) {
+                kn = k_frag(kcur, kb0, st + 1);
+                vn = v_frag(vcur, vb, st + 1);
+            }
+            if (st % NKK == 0) ns.h[st / NKK] = f32x16{};
+            ns.h[st / NKK] = mfma8(kfr, qf[st % NKK], ns.h[st / NKK]);
+            o[st] = mfma8(vfr, pcur, o[st]);
 #pragma unroll
             for (int q = 0; q < 8 / NDT; ++q) {
                 softmax_dw(cs, pnxt, st * (8 / NDT) + q, ct);
@@ -427,6 +444,8 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
                 asm volatile("" :: "v"(pnxt[st * (8 / NDT) + q]));
             }
             __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
+            kfr = kn;
+            vfr = vn;
         }
         sum_mfma(pcur);
         if (changed) rescale(alpha);  // after the products under the old reference
@@ -461,26 +480,26 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
 
     int32_t j = 0;
     for (; j + 3 < n_tiles; j += 2) {
-        full_iteration(j, sy, sx, Ks[0], Ks[1], Vs[0], Vs[1], pb[0], pb[1]);
-        full_iteration(j + 1, sx, sy, Ks[1], Ks[0], Vs[1], Vs[0], pb[1], pb[0]);
+        full_iteration(j, sy, sx, Ks0, Ks1, Vs0, Vs1, pb[0], pb[1]);
+        full_iteration(j + 1, sx, sy, Ks1, Ks0, Vs1, Vs0, pb[1], pb[0]);
     }
     if (j + 2 < n_tiles) {  // j even
-        full_iteration(j, sy, sx, Ks[0], Ks[1], Vs[0], Vs[1], pb[0], pb[1]);
+        full_iteration(j, sy, sx, Ks0, Ks1, Vs0, Vs1, pb[0], pb[1]);
         ++j;
     }
     // The last one or two tiles; every branch names its buffers statically.
     if (j + 1 < n_tiles) {
         if (j & 1) {
-            tail_iteration(sx, Vs[1], Vs[0], pb[1], pb[0]);
-            pv(Vs[0], pb[0]);
+            tail_iteration(sx, Vs1, Vs0, pb[1], pb[0]);
+            pv(Vs0, pb[0]);
         } else {
-            tail_iteration(sy, Vs[0], Vs[1], pb[0], pb[1]);
-            pv(Vs[1], pb[1]);
+            tail_iteration(sy, Vs0, Vs1, pb[0], pb[1]);
+            pv(Vs1, pb[1]);
         }
     } else if (j & 1) {
-        pv(Vs[1], pb[1]);
+        pv(Vs1, pb[1]);
     } else {
-        pv(Vs[0], pb[0]);
+        pv(Vs0, pb[0]);
     }
 
     if (!qvalid) return;
