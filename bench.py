@@ -22,12 +22,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: 256 CU x 8192 FLOP/clk x 2.4 GHz
-KERNEL_SRC = os.path.join(ROOT, "long_context_exact_ra_amd", "csrc", "fwd_bf16.hip")
+CSRC = os.path.join(ROOT, "long_context_exact_ra_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "fwd_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_share_L128K_N8.json")
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(src: str = KERNEL_SRC) -> str:
+    """sha256[:16] of the source file that holds the timed kernel."""
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -188,6 +190,8 @@ def main():
 
     if args.fp8 and args.backward:
         raise SystemExit("--fp8 times the forward share (optionally --causal) only")
+    timed_src = os.path.join(
+        CSRC, "fwd_fp8.hip" if args.fp8 else "bwd_bf16.hip" if args.backward else "fwd_bf16.hip")
     extra = {}
     if args.fp8:
         T = ra.fp8_tiles(w.l)
@@ -397,7 +401,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity": parity,
-        "kernel_sha": kernel_sha(),
+        "kernel_source": os.path.basename(timed_src),
+        "kernel_sha": kernel_sha(timed_src),
         "env": {"torch": torch.__version__, "hip": torch.version.hip,
                 "device": torch.cuda.get_device_name(0)},
     }
