@@ -19,6 +19,9 @@ Bounds: the forward uses the share's own bf16 bounds (test_gpu_parity.py). The b
 uses the magnitude bound of test_gpu_backward.py over the whole sequence. Each member's
 part of a key gradient stays within 2^-6 of its own magnitude sum, and those sums add up
 to the whole sequence's; the absolute floor grows to N * 1e-6.
+
+The FP8 causal share gets the same check against exact causal attention over the
+dequantized values in sequence order, within each member's own FP8 bound.
 """
 import math
 
@@ -27,9 +30,11 @@ import pytest
 import torch
 
 import oracle
-from long_context_exact_ra_amd import ra
+import oracle.fp8 as ofp8
+from long_context_exact_ra_amd import ra, synth
 from test_gpu_backward import TOL, _bits, _draw, magnitudes
 from test_gpu_causal_backward import masked_magnitudes
+from test_gpu_fp8 import run_fp8_share
 from test_gpu_parity import _say, check_O, check_stats
 
 pytestmark = pytest.mark.gpu
@@ -127,3 +132,57 @@ def test_members_together_are_the_whole_sequence(dev, case):
         worst[name] = w
     _say(f"whole ring {what}: O max abs err {err:.2e}; worst err/bound dQ {worst['dQ']:.3f} "
          f"dK {worst['dK']:.3f} dV {worst['dV']:.3f}")
+
+
+# ------------------------------------------------------------------ FP8 causal share
+
+# (layout, B, H, H_kv, d, N, l): GQA, both head sizes, a ragged striped block
+FP8_CASES = [
+    ("contiguous", 1, 2, 1, 128, 3, 256),
+    ("striped", 1, 2, 2, 64, 4, 200),
+    ("zigzag", 1, 2, 2, 128, 4, 256),
+    ("zigzag", 2, 2, 1, 64, 2, 384),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fp8_causal_members_together_are_the_whole_sequence(dev, case):
+    """Every member's FP8 causal share (GPU quantization and kernel) against exact causal
+    attention over the dequantized values of the whole sequence in its own order (one
+    member, no layout). The allowed deviation is the FP8 share's own bound
+    (oracle.fp8.error_bounds, which measures from that exact attention), per member."""
+    layout, B, H, H_kv, d, N, l = case
+    L = N * l
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = synth.draw(B, H, H_kv, d, L, L, "bf16", 7500 + l + N)
+    pos = oracle.layout_positions(layout, N, L)
+    take = torch.from_numpy(pos)
+    qm, km, vm = (x[:, :, take].contiguous() for x in (q, k, v))
+    O = np.empty((B, H, L, d))
+    Qd = np.empty((B, H, L, d))
+    for rank in range(N):
+        rows = slice(rank * l, (rank + 1) * l)
+        qr = qm[:, :, rows].contiguous()
+        (Or, _, _, _), _ = run_fp8_share(qr, km, vm, N, rank, scale, dev, layout=layout)
+        O[:, :, rows] = Or.double().cpu().numpy()
+        q8, qs = ofp8.quantize_rows(_bits(qr), 1, l)
+        Qd[:, :, rows] = ofp8.dequantize_rows(q8, qs, l)
+    k8, ks = ofp8.quantize_rows(_bits(km), N, l)
+    v8, vs = ofp8.quantize_vt(_bits(vm), N, l)
+    Kd, Vd = ofp8.dequantize_rows(k8, ks, l), ofp8.dequantize_vt(v8, vs, l)
+    back = np.argsort(pos)
+    ref, _, _ = oracle.causal_share(Qd[:, :, back], Kd[:, :, back], Vd[:, :, back], scale, 0, 1,
+                                    "contiguous")
+    ref = ref.reshape(B, H, L, d)[:, :, pos]  # member-major rows
+    worst = 0.0
+    for rank in range(N):
+        rows = slice(rank * l, (rank + 1) * l)
+        ref_r = ref[:, :, rows].reshape(-1, d)
+        bound, _, _ = ofp8.error_bounds(Qd[:, :, rows], Kd, Vd, scale, rank, N, ref_r,
+                                        np.arange(B * H * l), layout=layout)
+        got = O[:, :, rows].reshape(-1, d)
+        assert np.isfinite(got).all()
+        w = (np.abs(got - ref_r) / bound).max()
+        assert w <= 1.0, f"fp8 {case} rank {rank}: err/bound {w:.3f}"
+        worst = max(worst, w)
+    _say(f"whole ring fp8 {case}: worst O err/bound {worst:.3f}")
