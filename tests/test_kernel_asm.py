@@ -33,13 +33,21 @@ pytestmark = pytest.mark.skipif(
     reason="hipcc is needed to compile the kernels")
 
 
-def assembly(src, tmp_path):
-    out = tmp_path / (src + ".s")
-    cmd = [rabuild.hipcc(), *rabuild.common_flags(src), "--cuda-device-only", "-S", "-x", "hip",
-           os.path.join(rabuild.CSRC, src), "-o", str(out)]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr[-2000:]
-    return out.read_text()
+@pytest.fixture(scope="module")
+def assembly(tmp_path_factory):
+    """assembly(src): the gfx950 assembly of a kernel source, compiled once per module."""
+    cache = {}
+
+    def get(src):
+        if src not in cache:
+            out = tmp_path_factory.mktemp("asm") / (src + ".s")
+            cmd = [rabuild.hipcc(), *rabuild.common_flags(src), "--cuda-device-only", "-S",
+                   "-x", "hip", os.path.join(rabuild.CSRC, src), "-o", str(out)]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            assert res.returncode == 0, res.stderr[-2000:]
+            cache[src] = out.read_text()
+        return cache[src]
+    return get
 
 
 def loop_instructions(asm):
@@ -66,8 +74,8 @@ def loop_instructions(asm):
 
 
 @pytest.mark.parametrize("src", HOT)
-def test_loop_waits_for_tile_loads_only_at_the_barrier(src, tmp_path):
-    asm = assembly(src, tmp_path)
+def test_loop_waits_for_tile_loads_only_at_the_barrier(src, assembly):
+    asm = assembly(src)
     loops, bad = 0, []
     for kernel, block, body in loop_instructions(asm):
         loops += 1
@@ -81,8 +89,8 @@ def test_loop_waits_for_tile_loads_only_at_the_barrier(src, tmp_path):
 
 
 @pytest.mark.parametrize("src", HOT)
-def test_no_scratch_traffic_in_loops(src, tmp_path):
-    asm = assembly(src, tmp_path)
+def test_no_scratch_traffic_in_loops(src, assembly):
+    asm = assembly(src)
     bad = [f"{kernel[:60]} {block}: {ins}" for kernel, block, body in loop_instructions(asm)
            for ins in body if ins.startswith("scratch_") or "off, s[0:3]" in ins]
     assert not bad, "scratch access inside loops:\n" + "\n".join(bad[:10])
