@@ -94,3 +94,27 @@ def test_no_scratch_traffic_in_loops(src, assembly):
     bad = [f"{kernel[:60]} {block}: {ins}" for kernel, block, body in loop_instructions(asm)
            for ins in body if ins.startswith("scratch_") or "off, s[0:3]" in ins]
     assert not bad, "scratch access inside loops:\n" + "\n".join(bad[:10])
+
+
+def kernel_registers(asm):
+    """{kernel name: (vgpr_count, agpr_count)} from the code object metadata."""
+    meta = asm[asm.find("amdhsa.kernels"):]
+    out = {}
+    for blk in meta.split("  - .agpr_count:")[1:]:
+        agpr = int(blk.split("\n")[0].strip())
+        name = re.search(r"\.name:\s+(\S+)", blk).group(1)
+        vgpr = int(re.search(r"\.vgpr_count:\s+(\d+)", blk).group(1))
+        out[name] = (vgpr, agpr)
+    return out
+
+
+@pytest.mark.parametrize("src", HOT)
+def test_occupancy(src, assembly):
+    """Two waves per SIMD (an 8-wave work-group per CU) for the forward, FP8 and dQ kernels:
+    at most 256 registers per lane, VGPRs and AGPRs together. The dK/dV kernel runs one
+    wave per SIMD by design and may use all 512."""
+    regs = {k: v for k, v in kernel_registers(assembly(src)).items() if "prep" not in k}
+    assert regs, "no kernels found in the metadata"
+    for name, (vgpr, agpr) in regs.items():
+        limit = 512 if "dkdv" in name else 256
+        assert vgpr <= limit, f"{name}: {vgpr} registers (VGPR + AGPR), limit {limit}"
