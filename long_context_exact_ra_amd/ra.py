@@ -169,6 +169,12 @@ def make_shape(Q_i: torch.Tensor, K_blk: torch.Tensor | None = None) -> RaShape:
             raise ValueError("K block does not match Q_i")
         if K_blk.stride(3) != 1 or K_blk.stride(2) != d:
             raise ValueError("K/V block rows must be contiguous [.., l_kv, d]")
+        # The library reads a stride of 0 as "contiguous default", so a broadcast
+        # (expanded) head or batch axis would be taken for separate heads past the
+        # tensor's end: refuse it; the caller materialises such a block.
+        if (H_kv > 1 and K_blk.stride(1) == 0) or (B > 1 and K_blk.stride(0) == 0):
+            raise ValueError("K/V block must not be broadcast along heads or batch "
+                             "(stride 0); pass a materialised block")
         s.H_kv, s.l_kv = H_kv, l_kv
         s.kv_head_stride, s.kv_batch_stride = K_blk.stride(1), K_blk.stride(0)
     return s

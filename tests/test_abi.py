@@ -156,6 +156,27 @@ def test_binding_refuses_host_tensors():
         ra.share_forward(0, 4, 16, 2, 2, 64, 1, q, k, k, 0.125, o)
 
 
+def test_binding_refuses_broadcast_kv_blocks():
+    """A stride of 0 means 'contiguous default' to the library, so an expanded K/V
+    block (one head or batch entry broadcast) must be refused by the binding rather
+    than read as separate heads past the tensor's end."""
+    import torch
+    q = torch.zeros((2, 4, 8, 64), dtype=torch.bfloat16)
+    k = torch.zeros((2, 2, 16, 64), dtype=torch.bfloat16)
+    heads = k[:, :1].expand(2, 2, 16, 64)
+    batch = k[:1].expand(2, 2, 16, 64)
+    for blk in (heads, batch):
+        with pytest.raises(ValueError):
+            ra.make_shape(q, blk)
+        with pytest.raises(ValueError):
+            ra.step(q, blk, blk, None, None, None, 0.125)
+    # a single head (or batch entry) broadcast over nothing is still a valid block
+    one = torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16)
+    s = ra.make_shape(torch.zeros((1, 4, 8, 64), dtype=torch.bfloat16),
+                      one.expand(1, 1, 16, 64))
+    assert s.H_kv == 1 and s.l_kv == 16
+
+
 def test_bf16_heads_beyond_the_32_bit_buffer_range_are_unsupported():
     # One bf16 K/V head of 2^23 rows x 128 dims is 2^31 bytes: past the kernel's
     # 32-bit buffer range, refused before any device call.
