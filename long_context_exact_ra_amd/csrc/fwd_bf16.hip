@@ -191,6 +191,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     // Running state per lane (query row ln; lane halves hold different d / keys).
     f32x16 o[NDT];
     float lsum = 0.f;         // this half's partial row sum, relative to R
+    float tsum = 0.f;         // the same over the current tile only (blocked summation)
     float R = -INFINITY;      // exponent reference, log2 units
     float m_nat = -INFINITY;  // exact running max of scale * S
 #pragma unroll
@@ -382,7 +383,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c, nR));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i + 1], c, nR));
             const bf16x2 pk = {(bf16)p0, (bf16)p1};
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(ones, pk, lsum, false);
+            // Each tile's 16 probabilities per lane are summed on their own and the tile
+            // sum is then added to the running sum: the rounding error grows with the
+            // number of tiles, not the number of keys.
+            tsum = __builtin_amdgcn_fdot2_f32_bf16(ones, pk, (part | e) == 0 ? 0.f : tsum, false);
             pb[part][e] = pk[0];
             pb[part][e + 1] = pk[1];
         }
@@ -460,6 +464,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         if (changed) rescale_output(alpha);
 #pragma unroll
         for (int part = 0; part < NSTAGE; ++part) softmax_part(sx, pp, part);
+        lsum += tsum;
         if (n_tiles > 1) scores_full(K1, sy);
     }
     __syncthreads();  // every wave is done with K buffer 0
@@ -493,6 +498,11 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             pv_part(vcur, pp, stage);
             softmax_part(cs, pp, stage);  // P(j+1) replaces P(j) after its product
         }
+        lsum += tsum;
+        // Keep the numerators of tile j+1 in this block.  Left alone, the compiler sinks
+        // them past the rescale branch into the next iteration's block, so every other
+        // block has all the exponentials and the others have none beside their products.
+        asm volatile("" ::"v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(lsum));
         if (changed) rescale_output(alpha);  // after the old-reference products
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
         __syncthreads();
@@ -510,6 +520,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             pv_part(vcur, pp, stage);
             softmax_part(cs, pp, stage);
         }
+        lsum += tsum;
         if (changed) rescale_output(alpha);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
