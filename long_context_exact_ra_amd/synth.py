@@ -115,3 +115,22 @@ def sample_rows(B: int, H: int, q_rows: int, per_head: int, seed: int, tile: int
             out.extend((b * H + h) * q_rows + r for r in sorted(picks))
             i += 1
     return out
+
+
+def boundary_rows(B: int, H: int, q_rows: int, min_total: int, seed: int, tile: int = 256):
+    """Flat row indices (b*H + h)*q_rows + r, sorted, covering in every (batch, head) the
+    first and last row and both sides of every `tile` boundary, topped up with seeded
+    random rows (spread evenly over the heads) until there are at least `min_total`."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed) + 11)
+    n_heads = B * H
+    per_head = -(-max(min_total, 1) // n_heads)
+    out = []
+    for bh in range(n_heads):
+        picks = {0, q_rows - 1}
+        for t in range(tile, q_rows, tile):
+            picks.update((t - 1, t))
+        target = min(q_rows, max(per_head, len(picks)))
+        while len(picks) < target:
+            picks.add(int(torch.randint(0, q_rows, (1,), generator=g)))
+        out.extend(bh * q_rows + r for r in sorted(picks))
+    return out

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 from long_context_exact_ra_amd import ra, synth
+from bounds import stat_bounds_bf16
 from test_gpu_parity import _say, check_O, check_stats, flat_rows, host
 
 pytestmark = pytest.mark.gpu
@@ -83,7 +84,10 @@ def test_bf16_small_every_rank(dev, layout, case):
         what = f"{layout} {case} rank {rank}"
         err = check_O(O.cpu().numpy().reshape(Or.shape), Or, "bf16", what)
         check_O(cast.float().cpu().numpy().reshape(Or.shape), Or, "bf16", what + " cast")
-        check_stats(m.cpu().numpy().ravel(), lo.cpu().numpy().ravel(), M, Z, "bf16", what)
+        Qh = synth.to_oracle_array(qi)
+        bnd = stat_bounds_bf16(Qh, K, (B, H, H_kv, d, l, N * l), scale, np.arange(B * H * l), M)
+        check_stats(m.cpu().numpy().ravel(), lo.cpu().numpy().ravel(), M, Z, "bf16", what,
+                    bounds=bnd)
         _say(f"causal bf16 {what}: max abs err {err:.2e}")
 
 
@@ -111,7 +115,8 @@ def test_full_size_causal_sampled_rows(dev, layout):
         rows = synth.sample_rows(w.B, w.H, w.l, 8, w.seed + rank)
         Or, M, Z = oracle.causal_share(Q, K, V, scale, rank, w.N, layout, rows=rows)
         err = check_O(flat_rows(O, rows).cpu().numpy(), Or, "bf16", f"{layout} rank {rank}")
+        bnd = stat_bounds_bf16(Q, K, (w.B, w.H, w.H_kv, w.d, w.l, w.L), scale, rows, M)
         check_stats(flat_rows(m, rows).cpu().numpy(), flat_rows(lo, rows).cpu().numpy(), M, Z,
-                    "bf16", f"{layout} rank {rank}")
+                    "bf16", f"{layout} rank {rank}", bounds=bnd)
         assert torch.isfinite(O).all()
         _say(f"[causal {layout}] rank {rank}: max abs err {err:.2e} over {len(rows)} rows")

@@ -1,12 +1,16 @@
 """GPU parity of the HIP path against the fp64 CPU oracle, through the C ABI.
 
-Tolerances (written here, derived in the design notes):
-  fp32 inputs: max |O_gpu - O_ref| <= 1e-5.
-  bf16 inputs: |O_gpu - O_ref| <= 2e-2 + 1e-2 * |O_ref| elementwise.
-  Statistics: m to 1e-5 (fp32) / 1e-3 + 1e-5|m| (bf16); lse = m + ln l to 1e-5 (1 + |lse|)
-  (fp32) / ln(1 + 2^-8) ~ 3.9e-3 (bf16: the row sum adds the bf16-rounded probabilities
-  that also weight V, each within 2^-9 relative, with a 2x margin for fp32 score and
-  exp2 error).  The ring schedule trace must match bit-exactly.
+Tolerances:
+  fp32 inputs: max |O_gpu - O_ref| <= 1e-5 (the target's own bar).
+  bf16 inputs: |O_gpu - O_ref| <= 2e-2 + 1e-2 * |O_ref| elementwise (the target's own bar).
+  Row statistics (this build's outputs; no bar is given for them):
+    fp32: m and lse = m + ln l to 1e-5 (1 + |x|);
+    bf16: per-row bounds derived from the kernel's arithmetic in tests/bounds.py: the
+    bf16 rounding of the summed probabilities (2^-8 relative, worst case all one way),
+    the fp32 row-sum accumulation, the score error of the matrix instruction (its
+    grouped truncation is pinned in tests/test_gpu_accumulation.py), the exponent
+    argument's roundings and exp2's error.
+  The ring schedule trace must match bit-exactly.
 """
 import math
 import sys
@@ -17,10 +21,9 @@ import torch
 
 import oracle
 from long_context_exact_ra_amd import ra, synth
+from bounds import stat_bounds_bf16
 
 pytestmark = pytest.mark.gpu
-
-LSE_TOL_BF16 = math.log1p(2.0 ** -8)
 
 
 def _say(msg):
@@ -50,7 +53,9 @@ def check_O(gpu, ref, dtype, what=""):
     return float(err.max())
 
 
-def check_stats(m_gpu, l_gpu, M, Z, dtype, what=""):
+def check_stats(m_gpu, l_gpu, M, Z, dtype, what="", bounds=None):
+    """m and lse = m + ln l against the exact row maximum M and M + ln Z; for bf16,
+    `bounds` = (bound_m, bound_lse) per row from stat_bounds_bf16."""
     m_gpu = np.asarray(m_gpu, np.float64)
     lse_gpu = m_gpu + np.log(np.asarray(l_gpu, np.float64))
     lse = M + np.log(Z)
@@ -58,10 +63,11 @@ def check_stats(m_gpu, l_gpu, M, Z, dtype, what=""):
         assert np.all(np.abs(m_gpu - M) <= 1e-5 * (1 + np.abs(M))), what
         assert np.all(np.abs(lse_gpu - lse) <= 1e-5 * (1 + np.abs(lse))), what
     else:
-        assert np.all(np.abs(m_gpu - M) <= 1e-3 + 1e-5 * np.abs(M)), \
-            f"{what}: m err {np.abs(m_gpu - M).max():.3e}"
-        assert np.all(np.abs(lse_gpu - lse) <= LSE_TOL_BF16), \
-            f"{what}: lse err {np.abs(lse_gpu - lse).max():.3e}"
+        b_m, b_lse = bounds
+        em, el = np.abs(m_gpu - M), np.abs(lse_gpu - lse)
+        assert np.all(em <= b_m), f"{what}: m err/bound {(em / b_m).max():.3f}"
+        assert np.all(el <= b_lse), f"{what}: lse err/bound {(el / b_lse).max():.3f}"
+        return float((em / b_m).max()), float((el / b_lse).max())
 
 
 def dt_name(t):
@@ -162,9 +168,12 @@ def test_bf16_share_small(dev, B, H, H_kv, d, L, N, rank):
     err = check_O(O.cpu().numpy().reshape(Or.shape), Or, "bf16", "O")
     check_O(cast.float().cpu().numpy().reshape(Or.shape), Or, "bf16", "O_cast")
     assert torch.equal(cast, O.to(torch.bfloat16))
-    check_stats(m.cpu().numpy().ravel(), lo.cpu().numpy().ravel(), M, Z, "bf16")
+    bnd = stat_bounds_bf16(Q, K, (B, H, H_kv, d, l, L), scale, np.arange(B * H * l), M)
+    wm, wl = check_stats(m.cpu().numpy().ravel(), lo.cpu().numpy().ravel(), M, Z, "bf16",
+                         bounds=bnd)
     assert trace.cpu().tolist() == oracle.ring_schedule(rank, N)
-    _say(f"bf16 {B}x{H}/{H_kv} d{d} L{L} N{N} r{rank}: max abs err {err:.2e}")
+    _say(f"bf16 {B}x{H}/{H_kv} d{d} L{L} N{N} r{rank}: max abs err {err:.2e}, "
+         f"m err/bound {wm:.3f}, lse err/bound {wl:.3f}")
 
 
 @pytest.mark.parametrize("contiguous_blocks", [False, True])
@@ -188,7 +197,10 @@ def test_bf16_step_path_every_prefix(dev, contiguous_blocks):
         Op, Mp, Zp = oracle.share(Q, K, V, scale, rank, N, steps=t + 1)
         Og = (O_acc / lsum[..., None]).cpu().numpy().reshape(Op.shape)
         check_O(Og, Op, "bf16", f"step {t}")
-        check_stats(m.cpu().numpy().ravel(), lsum.cpu().numpy().ravel(), Mp, Zp, "bf16")
+        bnd = stat_bounds_bf16(Q, K, (B, H, H_kv, d, l, L), scale, np.arange(B * H * l), Mp,
+                               n_tiles=(t + 1) * -(-l // 64), n_steps=t + 1)
+        check_stats(m.cpu().numpy().ravel(), lsum.cpu().numpy().ravel(), Mp, Zp, "bf16",
+                    f"step {t}", bounds=bnd)
     cast = torch.empty((B, H, l, d), dtype=torch.bfloat16, device=dev)
     ra.finalize(O_acc, lsum, O_out=cast)
     torch.cuda.synchronize()
@@ -317,8 +329,9 @@ FULL = ["share_L32K_N8", "share_L128K_N8", "gqa_L128K_N8_28q4kv", "share_L1M_N64
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload_sampled_rows(dev, name):
-    """The launch the benchmark times, at full size; sampled rows against the oracle
-    (every head, first/last rows and both sides of query-tile boundaries)."""
+    """The launch the benchmark times, at full size, against the oracle on at least 4096
+    rows: in every head the first and last row and both sides of every 256-row query-tile
+    boundary, topped up with seeded random rows."""
     w = synth.WORKLOADS[name]
     _say(f"[{name}] drawing inputs")
     q, k, v = synth.draw_workload(w)
@@ -326,18 +339,24 @@ def test_full_size_workload_sampled_rows(dev, name):
     _say(f"[{name}] running share rank {w.rank} of {w.N}")
     O, m, lo, cast, trace = run_share(q.to(dev), k.to(dev), v.to(dev), w.rank, w.N, scale)
     assert trace.cpu().tolist() == oracle.ring_schedule(w.rank, w.N)
-    per_head = 16 if w.H * w.L <= 32 * 131072 else 12
-    rows = synth.sample_rows(w.B, w.H, w.l, per_head, w.seed)
-    Q, K, V = host(q, k, v)
-    _say(f"[{name}] oracle on {len(rows)} rows")
-    Or, M, Z = oracle.share(Q, K, V, scale, w.rank, w.N, rows=rows)
-    Og = flat_rows(O, rows).cpu().numpy()
-    err = check_O(Og, Or, "bf16", name)
-    check_O(flat_rows(cast, rows).float().cpu().numpy(), Or, "bf16", name + " cast")
-    check_stats(flat_rows(m, rows).cpu().numpy(), flat_rows(lo, rows).cpu().numpy(), M, Z,
-                "bf16", name)
     assert torch.isfinite(O).all()
-    _say(f"[{name}] max abs err {err:.2e} over {len(rows)} rows")
+    rows = synth.boundary_rows(w.B, w.H, w.l, 4096, w.seed)
+    Q, K, V = host(q, k, v)
+    Og, cg = flat_rows(O, rows).cpu().numpy(), flat_rows(cast, rows).float().cpu().numpy()
+    mg, lg = flat_rows(m, rows).cpu().numpy(), flat_rows(lo, rows).cpu().numpy()
+    worst = [0.0, 0.0, 0.0]
+    for i0 in range(0, len(rows), 1024):
+        part = rows[i0:i0 + 1024]
+        _say(f"[{name}] oracle on rows {i0}..{i0 + len(part) - 1} of {len(rows)}")
+        Or, M, Z = oracle.share(Q, K, V, scale, w.rank, w.N, rows=part)
+        sl = slice(i0, i0 + len(part))
+        err = check_O(Og[sl], Or, "bf16", name)
+        check_O(cg[sl], Or, "bf16", name + " cast")
+        bnd = stat_bounds_bf16(Q, K, (w.B, w.H, w.H_kv, w.d, w.l, w.L), scale, part, M)
+        wm, wl = check_stats(mg[sl], lg[sl], M, Z, "bf16", name, bounds=bnd)
+        worst = [max(worst[0], err), max(worst[1], wm), max(worst[2], wl)]
+    _say(f"[{name}] {len(rows)} rows: max abs err {worst[0]:.2e}, m err/bound "
+         f"{worst[1]:.3f}, lse err/bound {worst[2]:.3f}")
 
 
 def test_share_32k_every_row(dev):
@@ -362,7 +381,8 @@ def test_share_32k_every_row(dev):
         Or, M, Z = oracle.share(Q, K, V, scale, w.rank, w.N, rows=rows)
         err = check_O(Og[rows], Or, "bf16", f"32K rows {r0}+")
         check_O(cg[rows], Or, "bf16", f"32K cast rows {r0}+")
-        check_stats(mg[rows], lg[rows], M, Z, "bf16", f"32K rows {r0}+")
+        bnd = stat_bounds_bf16(Q, K, (w.B, w.H, w.H_kv, w.d, w.l, w.L), scale, rows, M)
+        check_stats(mg[rows], lg[rows], M, Z, "bf16", f"32K rows {r0}+", bounds=bnd)
         worst = max(worst, err)
         _say(f"[32K every row] rows {r0}..{r0 + len(rows) - 1}: max abs err {err:.2e}")
     _say(f"[32K every row] all {n} rows: max abs err {worst:.2e}")
