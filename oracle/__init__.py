@@ -44,6 +44,7 @@ online_step(...)
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -334,42 +335,49 @@ def share_backward_rows(Q, K, V, dO, scale, heads, q_rows, k_rows, chunk: int = 
     report for each of them.  Returns, per head, (dQ[q_rows] [nq, d], dK_part[k_rows],
     dV_part[k_rows]) where the K/V parts are this query head's contribution only.
     Same formulas as share_backward, evaluated in query chunks (with `layout`, each
-    chunk's scores are restricted to the admissible keys as in causal_share)."""
+    chunk's scores are restricted to the admissible keys as in causal_share), with
+    plain PyTorch CPU operations in float64 so that the elementwise work of a 128K share
+    runs on every host core."""
+    import torch
+
     q_all, k_all, v_all, do_all = Q, K, V, dO
     H = q_all.shape[1]
     H_kv = k_all.shape[1]
     g = H // H_kv
     qpos = kpos = None
     if layout is not None:
-        qpos = token_positions(layout, rank, N, q_all.shape[2])
-        kpos = layout_positions(layout, N, k_all.shape[2])
+        qpos = torch.from_numpy(token_positions(layout, rank, N, q_all.shape[2]))
+        kpos = torch.from_numpy(layout_positions(layout, N, k_all.shape[2]))
+    kr = torch.as_tensor(np.asarray(k_rows, dtype=np.int64))
+    qr = np.asarray(q_rows, dtype=np.int64)
     out = []
     for (b, h) in heads:
-        q = _f64(q_all[b, h])
-        k = _f64(k_all[b, h // g])
-        v = _f64(v_all[b, h // g])
-        do = _f64(do_all[b, h])
+        q = torch.from_numpy(_f64(q_all[b, h]))
+        k = torch.from_numpy(_f64(k_all[b, h // g]))
+        v = torch.from_numpy(_f64(v_all[b, h // g]))
+        do = torch.from_numpy(_f64(do_all[b, h]))
         l = q.shape[0]
-        kr = np.asarray(k_rows, dtype=np.int64)
-        dK = np.zeros((kr.size, q.shape[1]))
-        dV = np.zeros_like(dK)
-        dQ = np.zeros((len(q_rows), q.shape[1]))
-        qset = {int(r): i for i, r in enumerate(q_rows)}
+        dK = torch.zeros((kr.numel(), q.shape[1]), dtype=torch.float64)
+        dV = torch.zeros_like(dK)
+        dQ = torch.zeros((len(qr), q.shape[1]), dtype=torch.float64)
         for c0 in range(0, l, chunk):
             c1 = min(l, c0 + chunk)
+            sel = np.nonzero((qr >= c0) & (qr < c1))[0]
+            if kr.numel() == 0 and sel.size == 0:
+                continue  # this chunk adds nothing that was asked for
             S = scale * (q[c0:c1] @ k.T)
             if qpos is not None:
-                S = np.where(kpos[None, :] <= qpos[c0:c1, None], S, -np.inf)
-            P = np.exp(S - S.max(axis=1, keepdims=True))
-            P /= P.sum(axis=1, keepdims=True)
+                S = torch.where(kpos[None, :] <= qpos[c0:c1, None], S,
+                                torch.tensor(-math.inf, dtype=torch.float64))
+            P = torch.exp(S - S.max(dim=1, keepdim=True).values)
+            P /= P.sum(dim=1, keepdim=True)
             dP = do[c0:c1] @ v.T
-            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dS = P * (dP - torch.sum(P * dP, dim=1, keepdim=True))
             dV += P[:, kr].T @ do[c0:c1]
             dK += scale * (dS[:, kr].T @ q[c0:c1])
-            for r in range(c0, c1):
-                if r in qset:
-                    dQ[qset[r]] = scale * (dS[r - c0] @ k)
-        out.append((dQ, dK, dV))
+            if sel.size:
+                dQ[torch.from_numpy(sel)] = scale * (dS[torch.from_numpy(qr[sel] - c0)] @ k)
+        out.append((dQ.numpy(), dK.numpy(), dV.numpy()))
     return out
 
 
