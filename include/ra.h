@@ -47,7 +47,9 @@ typedef enum ra_status {
     RA_OK = 0,
     RA_EINVAL = 1,  /* bad argument; nothing was enqueued */
     RA_ENOTSUP = 2, /* current device is not gfx950, or an unsupported size */
-    RA_EHIP = 3     /* a HIP runtime call failed; see ra_last_hip_error() */
+    RA_EHIP = 3,    /* a HIP runtime call failed; see ra_last_hip_error() */
+    RA_ESCRATCH = 4 /* ra_share_backward_noalloc: the problem needs more than
+                       RA_NOALLOC_SCRATCH_BYTES of workspace; nothing was enqueued */
 } ra_status;
 
 typedef enum ra_dtype {
@@ -242,6 +244,30 @@ int ra_causal_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int3
 /* Bytes of workspace ra_share_backward (and ra_causal_share_backward) needs for B x H query rows of length l_q:
  * 8 * B * H * l_q (two floats per row).  Returns -RA_EINVAL for negative sizes. */
 int64_t ra_share_backward_workspace(int32_t B, int32_t H, int64_t l_q);
+
+/* Size of the static device scratch of ra_share_backward_noalloc: 8 MiB per GPU, enough
+ * for B * H * l <= 1048576 query rows (the 128K / N = 8, H = 32 share needs 524288). */
+#define RA_NOALLOC_SCRATCH_BYTES (8 << 20)
+
+/*
+ * ra_share_backward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as ra_share_backward, without `workspace`: the per-row workspace
+ * lives in a static device array of RA_NOALLOC_SCRATCH_BYTES that each GPU holds from
+ * the first call on it until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).
+ *   - A problem whose ra_share_backward_workspace(B, H, L / N) exceeds
+ *     RA_NOALLOC_SCRATCH_BYTES returns RA_ESCRATCH, after the usual argument checks and
+ *     before any device work.
+ *   - The array is shared by every call on one GPU and keeps the last call's contents
+ *     (each call writes every entry it reads, so nothing needs clearing).  Calls that
+ *     overlap on one GPU (other streams, other host threads) race on it: serialise them.
+ */
+int ra_share_backward_noalloc(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                              int32_t d, int32_t B, int32_t dtype, const void *Q_i,
+                              const void *K, const void *V, const float *O, const void *dO,
+                              const float *m, const float *l, float scale, float *dQ,
+                              float *dK, float *dV, void *stream);
 
 /*
  * FP8 (OCP E4M3) inputs with block quantization (aliyun FlashAttention explainer,

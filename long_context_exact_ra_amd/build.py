@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libra.so")
 SOURCES = ["ra_api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "util.hip", "bwd_bf16.hip",
-           "fwd_fp8.hip", "fp8_quant.hip"]
+           "fwd_fp8.hip", "fp8_quant.hip", "noalloc.hip"]
 ARCH = "gfx950"
 NO_NAN_SOURCES = {"fwd_bf16.hip"}
 

@@ -5,6 +5,7 @@
 #include "../../include/ra.h"
 
 #include <atomic>
+#include <cstdint>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -138,11 +139,12 @@ int share_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, in
 }
 
 // Shared by ra_share_backward (layout kNoCausal) and ra_causal_share_backward.
+// With validate_only, it returns after the argument checks (no HIP call at all).
 int backward_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, int32_t d,
                     int32_t B, int32_t dtype, int32_t layout, const void *Q_i, const void *K,
                     const void *V, const float *O, const void *dO, const float *m,
                     const float *l, float scale, float *dQ, float *dK, float *dV,
-                    void *workspace, void *stream) {
+                    void *workspace, void *stream, bool validate_only = false) {
     if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0 ||
         !heads_ok(B, H, H_kv, d, dtype) || !scale_ok(scale))
         return RA_EINVAL;
@@ -162,6 +164,7 @@ int backward_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
     const int64_t kpb = (kblk + ra::bwd_key_tile() - 1) / ra::bwd_key_tile();
     const int64_t kt = kpb * nkb;
     if (qt * B * H > INT32_MAX || kt * B * H_kv > INT32_MAX) return RA_ENOTSUP;
+    if (validate_only) return RA_OK;
     int rc = check_device();
     if (rc != RA_OK) return rc;
     ra::BwdArgs a{};
@@ -402,6 +405,27 @@ int ra_causal_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int3
                            scale, dQ, dK, dV, workspace, stream);
 }
 
+int ra_share_backward_noalloc(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
+                              int32_t d, int32_t B, int32_t dtype, const void *Q_i,
+                              const void *K, const void *V, const float *O, const void *dO,
+                              const float *m, const float *l, float scale, float *dQ,
+                              float *dK, float *dV, void *stream) {
+    // Every argument check first, with a stand-in (aligned, never used) workspace address.
+    void *const stand_in = (void *)(uintptr_t)256;
+    int rc = backward_launch(rank, N, L, H, H_kv, d, B, dtype, ra::kNoCausal, Q_i, K, V, O,
+                             dO, m, l, scale, dQ, dK, dV, stand_in, stream, true);
+    if (rc != RA_OK || L == 0) return rc;
+    if (ra_share_backward_workspace(B, H, L / N) > (int64_t)RA_NOALLOC_SCRATCH_BYTES)
+        return RA_ESCRATCH;
+    rc = check_device();
+    if (rc != RA_OK) return rc;
+    void *scratch = nullptr;
+    const hipError_t e = ra::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e);
+    return backward_launch(rank, N, L, H, H_kv, d, B, dtype, ra::kNoCausal, Q_i, K, V, O, dO,
+                           m, l, scale, dQ, dK, dV, scratch, stream);
+}
+
 int64_t ra_fp8_tiles(int64_t seg) {
     if (seg < 0) return -RA_EINVAL;
     return (seg + 63) / 64;
@@ -459,6 +483,9 @@ const char *ra_strerror(int status) {
     case RA_EINVAL: return "invalid argument";
     case RA_ENOTSUP: return "unsupported device or size (needs gfx950)";
     case RA_EHIP: return "HIP runtime error (see ra_last_hip_error)";
+    case RA_ESCRATCH:
+        return "problem too large for the allocation-free entry point's scratch "
+               "(RA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

@@ -130,6 +130,10 @@ hipError_t launch_quant_vt(const void *x, uint8_t *codes, float *descale, int64_
                            int32_t n_seg, int64_t seg, int d, hipStream_t st);
 hipError_t launch_state_init(float *O_acc, float *m, float *l, int64_t rows, int d,
                              hipStream_t st);
+
+// Device address, on the current device, of the library's static scratch array
+// (RA_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned), looked up once per device.
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_finalize(float *O_acc, const float *l, int64_t rows, int d, int dtype,
                            void *O_out, hipStream_t st);
 

@@ -14,7 +14,8 @@ import os
 
 import torch
 
-RA_OK, RA_EINVAL, RA_ENOTSUP, RA_EHIP = 0, 1, 2, 3
+RA_OK, RA_EINVAL, RA_ENOTSUP, RA_EHIP, RA_ESCRATCH = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 8 << 20
 RA_F32, RA_BF16 = 0, 1
 RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
 RA_FP8_ROWS, RA_FP8_VT = 0, 1
@@ -76,6 +77,9 @@ def load():
                                                     i32, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                                     vp, vp, vp, vp]),
         "ra_share_backward_workspace": (i64, [i32, i32, i64]),
+        "ra_share_backward_noalloc": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, i32,
+                                                     vp, vp, vp, vp, vp, vp, vp, f32, vp, vp,
+                                                     vp, vp]),
         "ra_fp8_tiles": (i64, [i64]),
         "ra_quantize_fp8": (ctypes.c_int, [i32, i32, i32, i32, i64, i32, vp, vp, vp, vp]),
         "ra_share_forward_fp8": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, vp, vp, vp,
@@ -98,6 +102,7 @@ def exported_symbols() -> list[str]:
     return ["ra_ring_block", "ra_ring_schedule", "ra_kv_head", "ra_state_init", "ra_step",
             "ra_finalize", "ra_share_forward", "ra_causal_share_forward", "ra_causal_pairs",
             "ra_share_backward", "ra_causal_share_backward", "ra_share_backward_workspace",
+            "ra_share_backward_noalloc",
             "ra_fp8_tiles", "ra_quantize_fp8", "ra_share_forward_fp8",
             "ra_causal_share_forward_fp8", "ra_strerror",
             "ra_last_hip_error"]
@@ -332,6 +337,32 @@ def share_backward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int,
     ra_share_backward_workspace bytes) is allocated here when not given."""
     _backward(rank, N, L, H, H_kv, d, B, None, Q_i, K, V, O, dO, m, l, scale, dQ, dK, dV,
               workspace, stream)
+
+
+def share_backward_noalloc(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int, Q_i,
+                           K, V, O, dO, m, l, scale: float, dQ, dK, dV, stream=None):
+    """share_backward without a workspace argument: the library's static scratch serves
+    (see ra_share_backward_noalloc in ra.h; raises RaError(RA_ESCRATCH) for problems
+    larger than NOALLOC_SCRATCH_BYTES of workspace)."""
+    if N < 1 or L % N != 0:
+        raise ValueError("L must be a multiple of N >= 1")
+    lq = L // N
+    dt = Q_i.dtype
+    _need_shape(Q_i, (B, H, lq, d), "Q_i")
+    _need_shape(K, (B, H_kv, L, d), "K", dt)
+    _need_shape(V, (B, H_kv, L, d), "V", dt)
+    _need_shape(O, (B, H, lq, d), "O", torch.float32)
+    _need_shape(dO, (B, H, lq, d), "dO", dt)
+    _need_shape(m, (B, H, lq), "m", torch.float32)
+    _need_shape(l, (B, H, lq), "l", torch.float32)
+    _need_shape(dQ, (B, H, lq, d), "dQ", torch.float32)
+    _need_shape(dK, (B, H_kv, L, d), "dK", torch.float32)
+    _need_shape(dV, (B, H_kv, L, d), "dV", torch.float32)
+    _check(load().ra_share_backward_noalloc(
+        rank, N, L, H, H_kv, d, B, _dtype_code(Q_i), _dev(Q_i, "Q_i"), _dev(K, "K"),
+        _dev(V, "V"), _dev(O, "O"), _dev(dO, "dO"), _dev(m, "m"), _dev(l, "l"), float(scale),
+        _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"), _stream(stream)),
+        "ra_share_backward_noalloc")
 
 
 def causal_share_backward(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int,

@@ -141,6 +141,12 @@ static void device_entry_points(char *p) {
                                          p, p, p, 0.1f, f, f, f, p, st), "zigzag odd chunks");
     EXPECT_INVAL(ra_share_backward(0, 8, 2048, 4, 2, 128, 1, RA_BF16, p, p, p, f, p, f, f, 0.1f,
                                    f, f, f, nullptr, st), "backward null workspace");
+    EXPECT_OK(ra_share_backward_noalloc(3, 8, 8 * 256, 4, 2, 128, 1, RA_BF16, p, p, p, f, p, f,
+                                        f, 0.1f, f, f, f, st), "backward noalloc");
+    CHECK(ra_share_backward_noalloc(0, 1, 65537, 16, 16, 128, 1, RA_BF16, p, p, p, f, p, f, f,
+                                    0.1f, f, f, f, st) == RA_ESCRATCH, "noalloc too large");
+    EXPECT_INVAL(ra_share_backward_noalloc(0, 8, 2048, 4, 2, 128, 1, RA_BF16, p, p, p, nullptr,
+                                           p, f, f, 0.1f, f, f, f, st), "noalloc null O");
     EXPECT_INVAL(ra_share_backward(0, 8, 2048, 4, 2, 128, 1, RA_BF16, p, p, p, nullptr, p, f, f,
                                    0.1f, f, f, f, p, st), "backward null O");
 

@@ -88,4 +88,10 @@ hipError_t launch_finalize(float *, const float *, int64_t rows, int d, int, voi
     ++g_launches;
     return hipSuccess;
 }
+// Stand-in for the static scratch lookup: a host buffer that the stub launches never read.
+alignas(256) static unsigned char g_scratch_stub[256];
+hipError_t noalloc_scratch(void **ptr) {
+    *ptr = g_scratch_stub;
+    return hipSuccess;
+}
 }  // namespace ra

@@ -349,3 +349,29 @@ def test_causal_share_forward_fp8_rejects(kw):
 
 def test_causal_share_forward_fp8_noop():
     assert _cfp8(L=0, Q=None, K=None, V=None, O=None) == ra.RA_OK
+
+
+# ------------------------------------------------------------------ allocation-free backward
+
+def test_backward_noalloc_rejects_before_device_work():
+    lib = ra.load()
+
+    def call(**kw):
+        a = dict(rank=0, N=4, L=1024, H=2, H_kv=2, d=128, B=1, dtype=ra.RA_BF16, scale=0.088)
+        a.update(kw)
+        return lib.ra_share_backward_noalloc(a["rank"], a["N"], a["L"], a["H"], a["H_kv"],
+                                             a["d"], a["B"], a["dtype"], P, P, P, P, P, P, P,
+                                             a["scale"], P, P, P, None)
+    assert call(N=0) == ra.RA_EINVAL
+    assert call(rank=4) == ra.RA_EINVAL
+    assert call(L=1000, N=3) == ra.RA_EINVAL
+    assert call(H=3, H_kv=2) == ra.RA_EINVAL
+    assert call(scale=float("nan")) == ra.RA_EINVAL
+    assert call(dtype=ra.RA_F32) == ra.RA_ENOTSUP
+    assert call(L=0) == ra.RA_OK
+    # 8 bytes per query row: 2^20 rows fit, one more query row per head does not
+    rows = ra.NOALLOC_SCRATCH_BYTES // 8
+    assert lib.ra_share_backward_workspace(1, 16, rows // 16) == ra.NOALLOC_SCRATCH_BYTES
+    assert call(H=16, H_kv=16, N=1, L=rows // 16 + 1) == ra.RA_ESCRATCH
+    assert call(B=2, H=64, H_kv=8, N=8, L=8 * 16384) == ra.RA_ESCRATCH
+    assert b"scratch" in lib.ra_strerror(ra.RA_ESCRATCH)
