@@ -229,3 +229,57 @@ def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows, layout=None)
         bl[i] = 2 * e.sum() + P @ np.expm1(ds + ds.max()) + acc * Z
     return bO, bm, bl
 
+
+
+# ------------------------------------------------------------------ incoherent processing
+#
+# The FlashAttention-3 paragraph of the aliyun explainer names a second remedy for the
+# error of FP8 products beside block quantization: incoherent processing, i.e. multiplying
+# Q and K by the same random orthogonal matrix along the head dimension before quantizing,
+# which leaves Q K^T unchanged and spreads any outlier channel over all of them.  The page
+# fixes neither the matrix nor the scaling; the reading taken here is the Sylvester
+# Hadamard matrix H_d (entries +-1, H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]) times a
+# diagonal of random signs S, unnormalised: (Q S H)(K S H)^T = d Q K^T, and the factor 1/d
+# (a power of two) goes into Q's descales, so the share over the quantized rotated inputs
+# uses the usual scale.
+
+
+def hadamard(d: int) -> np.ndarray:
+    """The Sylvester Hadamard matrix H_d (d a power of two), float64 entries +-1."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_rotate(x, signs) -> np.ndarray:
+    """x [..., d] (bf16 bits or float32) times diag(signs) H_d, in float32, by the fast
+    transform: after the sign flips (exact), for h = 1, 2, 4, ..., d/2 every pair of
+    entries (i, i + h) with i & h == 0 becomes (a + b, a - b), each a single float32
+    rounding.  (H_d is symmetric, so row vectors times H_d are H_d times columns.)"""
+    y = (_f32(x) * np.asarray(signs, dtype=np.float32)).astype(np.float32)
+    d = y.shape[-1]
+    if d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = 1
+    while h < d:
+        y = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a, b = y[..., 0, :], y[..., 1, :]
+        y = np.stack([(a + b).astype(np.float32), (a - b).astype(np.float32)], axis=-2)
+        y = y.reshape(y.shape[:-3] + (d,))
+        h *= 2
+    return y
+
+
+def quantize_rows_hadamard(x, signs, n_seg: int, seg: int, query_side: bool):
+    """Incoherent processing then block quantization: quantize_rows of
+    hadamard_rotate(x, signs); for the query side (query_side) the descales are
+    multiplied by 1/d (exact: a power of two), so that a share over Q and K quantized
+    this way needs no change of scale.  Returns (codes, descale) as quantize_rows."""
+    r = hadamard_rotate(x, signs)
+    codes, descale = quantize_rows(r, n_seg, seg)
+    if query_side:
+        descale = (descale * np.float32(1.0 / r.shape[-1])).astype(np.float32)
+    return codes, descale

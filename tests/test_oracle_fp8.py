@@ -243,3 +243,81 @@ def test_causal_share_fp8_equals_the_plain_causal_share_on_exact_inputs(layout):
         O, M, Z = oracle.causal_share(Q, K, V, 2.0 ** -15, rank, N, layout)
         np.testing.assert_allclose(O8, O, rtol=0, atol=1e-12 * np.abs(O).max())
         np.testing.assert_allclose(Z8, Z, rtol=1e-12)
+
+
+# ------------------------------------------------------------------ incoherent processing
+
+def test_hadamard_is_the_library_sylvester_matrix_and_orthogonal():
+    import scipy.linalg
+    for d in (1, 2, 4, 64, 128):
+        H = fp8.hadamard(d)
+        assert np.array_equal(H, scipy.linalg.hadamard(d))
+        assert np.array_equal(H @ H.T, d * np.eye(d))
+
+
+def test_fast_rotation_equals_the_matrix_product():
+    rng = np.random.default_rng(31)
+    signs = np.where(rng.random(128) < 0.5, -1.0, 1.0)
+    # small integers: every float32 sum is exact, so the transform must equal the product
+    x = rng.integers(-8, 9, size=(4, 7, 128)).astype(np.float32)
+    y = fp8.hadamard_rotate(x, signs)
+    assert np.array_equal(y, (x.astype(np.float64) * signs) @ fp8.hadamard(128))
+    # general values: within the rounding of 7 butterfly stages
+    x = rng.standard_normal((4, 7, 128)).astype(np.float32)
+    y = fp8.hadamard_rotate(x, signs)
+    ref = (x.astype(np.float64) * signs) @ fp8.hadamard(128)
+    assert np.all(np.abs(y - ref) <= 7 * 2.0 ** -24 * 2 * np.abs(x).sum(axis=-1, keepdims=True))
+
+
+def test_rotation_leaves_the_exact_share_unchanged():
+    """(Q S H)(K S H)^T = d Q K^T: the share over rotated Q, K with scale / d is the share."""
+    rng = np.random.default_rng(32)
+    B, H, d, l, N = 1, 2, 64, 16, 4
+    L = N * l
+    Q = rng.standard_normal((B, H, l, d))
+    K = rng.standard_normal((B, H, L, d))
+    V = rng.standard_normal((B, H, L, d))  # all three inputs float64
+    signs = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    R = signs[:, None] * fp8.hadamard(d)
+    O1, M1, Z1 = oracle.share(Q, K, V, 0.125, 1, N)
+    O2, M2, Z2 = oracle.share(Q @ R, K @ R, V, 0.125 / d, 1, N)
+    np.testing.assert_allclose(O2, O1, atol=1e-12)
+    np.testing.assert_allclose(M2 + np.log(Z2), M1 + np.log(Z1), atol=1e-12)
+
+
+def test_rotated_quantization_folds_one_over_d_into_query_descales():
+    rng = np.random.default_rng(33)
+    x = torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(5))
+    bits = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    signs = np.where(rng.random(128) < 0.5, -1.0, 1.0)
+    ck, dk = fp8.quantize_rows_hadamard(bits, signs, 1, 128, False)
+    cq, dq = fp8.quantize_rows_hadamard(bits, signs, 1, 128, True)
+    assert np.array_equal(ck, cq)
+    assert np.array_equal(dq, (dk / np.float32(128)).astype(np.float32))
+    r = fp8.hadamard_rotate(bits, signs)
+    rc, rd = fp8.quantize_rows(r, 1, 128)
+    assert np.array_equal(ck, rc) and np.array_equal(dk, rd)
+
+
+def test_rotation_spreads_an_outlier_channel():
+    """The point of incoherent processing: with one large channel in Q and K, the FP8
+    scores of the rotated pair are closer to the exact ones than without the rotation."""
+    g = torch.Generator().manual_seed(6)
+    d, n = 128, 256
+    q = torch.randn(1, 1, n, d, generator=g)
+    k = torch.randn(1, 1, n, d, generator=g)
+    q[..., 5] *= 40.0
+    k[..., 5] *= 40.0
+    qb, kb = (t.to(torch.bfloat16) for t in (q, k))
+    Qb, Kb = (t.view(torch.int16).numpy().view(np.uint16) for t in (qb, kb))
+    exact = qb.double()[0, 0].numpy() @ kb.double()[0, 0].numpy().T
+    cq, dq = fp8.quantize_rows(Qb, 1, n)
+    ck, dk = fp8.quantize_rows(Kb, 1, n)
+    plain = fp8.dequantize_rows(cq, dq, n)[0, 0] @ fp8.dequantize_rows(ck, dk, n)[0, 0].T
+    signs = np.where(np.random.default_rng(34).random(d) < 0.5, -1.0, 1.0)
+    cq, dq = fp8.quantize_rows_hadamard(Qb, signs, 1, n, True)
+    ck, dk = fp8.quantize_rows_hadamard(Kb, signs, 1, n, False)
+    rot = fp8.dequantize_rows(cq, dq, n)[0, 0] @ fp8.dequantize_rows(ck, dk, n)[0, 0].T
+    e_plain = np.abs(plain - exact).mean()
+    e_rot = np.abs(rot - exact).mean()
+    assert e_rot < 0.7 * e_plain, (e_rot, e_plain)
