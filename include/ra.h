@@ -302,6 +302,27 @@ int ra_quantize_fp8(int32_t kind, int32_t B, int32_t Hx, int32_t n_seg, int64_t 
                     const void *x, void *codes, float *descale, void *stream);
 
 /*
+ * Incoherent processing, then block quantization, for the query and key sides of the FP8
+ * share (aliyun FlashAttention explainer, section 2, FlashAttention-3: block quantization
+ * and incoherent processing limit the error of FP8 products).  Each row x of
+ * x [B, Hx, n_seg * seg, d] (bf16) becomes x diag(signs) H_d, H_d the Sylvester Hadamard
+ * matrix with entries +-1 (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), computed in fp32 by
+ * the fast transform (for h = 1, 2, ..., d/2, each pair of entries (i, i + h) with
+ * i & h == 0 becomes (a + b, a - b)), and is then quantized exactly as RA_FP8_ROWS does.
+ * Since (Q S H)(K S H)^T = d Q K^T, quantize Q with query_side = 1 (its descales are
+ * multiplied by 1/d, exact) and K with query_side = 0, with the same signs; the FP8 share
+ * over those inputs then takes the usual scale and computes the same attention.  V is
+ * quantized as before (RA_FP8_VT), unrotated.
+ *   signs   device fp32 [d], normally random +-1 (drawn by the caller; other values are
+ *           applied as given)
+ *   codes, descale  as ra_quantize_fp8 with RA_FP8_ROWS
+ * seg == 0 is a no-op.  Errors as ra_quantize_fp8 (RA_EINVAL also for a NULL signs).
+ */
+int ra_quantize_fp8_hadamard(int32_t B, int32_t Hx, int32_t n_seg, int64_t seg, int32_t d,
+                             const void *x, const float *signs, int32_t query_side,
+                             void *codes, float *descale, void *stream);
+
+/*
  * Rank `rank`'s non-causal share (as ra_share_forward) from FP8 inputs, products on the
  * gfx950 FP8 matrix path, fp32 statistics:
  *   Q8 [B, H, l, d] codes with q_descale [B, H, T(l)]          (RA_FP8_ROWS, n_seg = 1)

@@ -48,12 +48,22 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 }
 
 // One 64-row block per work-group (256 threads, 16-byte chunks of 8 values).
-template <int D>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, uint8_t *codes,
+// With ROT (incoherent processing), each row is first multiplied by diag(signs) H_D, H_D
+// the Sylvester Hadamard matrix (entries +-1), in fp32 by the fast transform: for
+// h = 1, 2, 4, ..., D/2 every pair of entries (i, i + h) with i & h == 0 becomes
+// (a + b, a - b).  A row's D values sit in D/8 consecutive lanes, 8 per lane, so the
+// stages h < 8 run inside a lane and the others pair lane L with lane L ^ (h / 8); each
+// entry goes through the same fp32 operations in the same order whichever lane computes
+// it.  The block is then quantized as without ROT, and its descale multiplied by `post`
+// (1, or 1/D for the query side: a power of two, exact).
+template <int D, bool ROT>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, const float *signs,
+                                                         float post, uint8_t *codes,
                                                          float *descale, int32_t n_seg,
                                                          int64_t seg, int32_t T) {
     constexpr int CPR = D / 8;               // chunks per row
     constexpr int PER = QT * CPR / 256;      // chunks per thread
+    static_assert(256 % CPR == 0, "a thread's chunks share their position in the row");
     __shared__ float red[4];
     const int64_t wg = blockIdx.x;
     const int u = (int)(wg % T);
@@ -64,33 +74,68 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, uint8_t 
     const int64_t left = seg - (int64_t)u * QT;
     const int nrows = left < QT ? (int)left : QT;
     const int64_t base = (hd * n_seg * seg + row0) * D;  // element offset of the block
+    const int c = threadIdx.x % CPR;                    // this thread's chunk of each row
 
-    bf16x8 v[PER];
-    float amax = 0.f;
+    float f[PER][8];
+    float sg[8];
+    if constexpr (ROT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sg[e] = signs[8 * c + e];
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int q = threadIdx.x + 256 * i;
-        const int r = q / CPR;
-        if (r < nrows) {
-            v[i] = *(const bf16x8 *)(x + base + (int64_t)q * 8);
+        if (q / CPR < nrows) {
+            const bf16x8 v = *(const bf16x8 *)(x + base + (int64_t)q * 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[i][e]));
+            for (int e = 0; e < 8; ++e) f[i][e] = ROT ? (float)v[e] * sg[e] : (float)v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[i][e] = 0.f;
         }
     }
+    if constexpr (ROT) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+#pragma unroll
+            for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (!(e & h)) {
+                        const float a = f[i][e], b = f[i][e + h];
+                        f[i][e] = a + b;
+                        f[i][e + h] = a - b;
+                    }
+#pragma unroll
+            for (int k = 1; k < CPR; k *= 2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float mine = f[i][e];
+                    const float other = __shfl_xor(mine, k);
+                    f[i][e] = (c & k) ? other - mine : mine + other;
+                }
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if ((threadIdx.x + 256 * i) / CPR < nrows)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[i][e]));
     const float ds = descale_of(block_max(amax, red));
     const float inv = 1.0f / ds;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int q = threadIdx.x + 256 * i;
         if (q / CPR < nrows) {
-            float f[8];
+            float g[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = (float)v[i][e] * inv;
+            for (int e = 0; e < 8; ++e) g[e] = f[i][e] * inv;
             *(u32x2 *)(codes + base + (int64_t)q * 8) =
-                u32x2{pack4(f[0], f[1], f[2], f[3]), pack4(f[4], f[5], f[6], f[7])};
+                u32x2{pack4(g[0], g[1], g[2], g[3]), pack4(g[4], g[5], g[6], g[7])};
         }
     }
-    if (threadIdx.x == 0) descale[hs * T + u] = ds;
+    if (threadIdx.x == 0) descale[hs * T + u] = ROT ? ds * post : ds;
 }
 
 __global__ void fill_zero_kernel(float *p, int64_t n) {
@@ -169,13 +214,14 @@ __global__ __launch_bounds__(256) void vt_quant_kernel(const bf16 *x, uint8_t *c
         *(u32x4 *)(op + 16 * k) = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
 }
 
-template <int D>
-hipError_t rows_impl(const void *x, uint8_t *codes, float *descale, int64_t heads,
-                     int32_t n_seg, int64_t seg, hipStream_t st) {
+template <int D, bool ROT>
+hipError_t rows_impl(const void *x, const float *signs, float post, uint8_t *codes,
+                     float *descale, int64_t heads, int32_t n_seg, int64_t seg,
+                     hipStream_t st) {
     const int32_t T = (int32_t)((seg + QT - 1) / QT);
     const int64_t n = heads * n_seg * T;
-    hipLaunchKernelGGL((quant_rows_kernel<D>), dim3((unsigned)n), dim3(256), 0, st,
-                       (const bf16 *)x, codes, descale, n_seg, seg, T);
+    hipLaunchKernelGGL((quant_rows_kernel<D, ROT>), dim3((unsigned)n), dim3(256), 0, st,
+                       (const bf16 *)x, signs, post, codes, descale, n_seg, seg, T);
     return hipGetLastError();
 }
 
@@ -205,8 +251,21 @@ hipError_t vt_impl(const void *x, uint8_t *codes, float *descale, int64_t heads,
 
 hipError_t launch_quant_rows(const void *x, uint8_t *codes, float *descale, int64_t heads,
                              int32_t n_seg, int64_t seg, int d, hipStream_t st) {
-    if (d == 128) return rows_impl<128>(x, codes, descale, heads, n_seg, seg, st);
-    if (d == 64) return rows_impl<64>(x, codes, descale, heads, n_seg, seg, st);
+    if (d == 128)
+        return rows_impl<128, false>(x, nullptr, 1.f, codes, descale, heads, n_seg, seg, st);
+    if (d == 64)
+        return rows_impl<64, false>(x, nullptr, 1.f, codes, descale, heads, n_seg, seg, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_rows_hadamard(const void *x, const float *signs, bool query_side,
+                                      uint8_t *codes, float *descale, int64_t heads,
+                                      int32_t n_seg, int64_t seg, int d, hipStream_t st) {
+    const float post = query_side ? 1.0f / (float)d : 1.0f;
+    if (d == 128)
+        return rows_impl<128, true>(x, signs, post, codes, descale, heads, n_seg, seg, st);
+    if (d == 64)
+        return rows_impl<64, true>(x, signs, post, codes, descale, heads, n_seg, seg, st);
     return hipErrorInvalidValue;
 }
 

@@ -454,6 +454,24 @@ int ra_quantize_fp8(int32_t kind, int32_t B, int32_t Hx, int32_t n_seg, int64_t 
     return after_launch(e, st);
 }
 
+int ra_quantize_fp8_hadamard(int32_t B, int32_t Hx, int32_t n_seg, int64_t seg, int32_t d,
+                             const void *x, const float *signs, int32_t query_side,
+                             void *codes, float *descale, void *stream) {
+    if (B < 1 || Hx < 1 || n_seg < 1 || seg < 0 || (d != 64 && d != 128)) return RA_EINVAL;
+    if (seg == 0) return RA_OK;
+    if (!ptr_ok(x) || !ptr_ok(signs) || !ptr_ok(codes) || !ptr_ok(descale)) return RA_EINVAL;
+    const int64_t heads = (int64_t)B * Hx;
+    const int64_t T = (seg + 63) / 64;
+    if (heads * n_seg * T > INT32_MAX) return RA_ENOTSUP;
+    int rc = check_device();
+    if (rc != RA_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    return after_launch(ra::launch_quant_rows_hadamard(x, signs, query_side != 0,
+                                                       (uint8_t *)codes, descale, heads, n_seg,
+                                                       seg, d, st),
+                        st);
+}
+
 int ra_share_forward_fp8(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
                          int32_t d, int32_t B, const void *Q8, const float *q_descale,
                          const void *K8, const float *k_descale, const void *V8t,

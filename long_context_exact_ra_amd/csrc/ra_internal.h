@@ -128,6 +128,11 @@ hipError_t launch_quant_rows(const void *x, uint8_t *codes, float *descale, int6
                              int32_t n_seg, int64_t seg, int d, hipStream_t st);
 hipError_t launch_quant_vt(const void *x, uint8_t *codes, float *descale, int64_t heads,
                            int32_t n_seg, int64_t seg, int d, hipStream_t st);
+// Rows mode after incoherent processing: each row times diag(signs) H_d (fp32 fast
+// Hadamard transform), then quantized; the query side's descales carry a factor 1/d.
+hipError_t launch_quant_rows_hadamard(const void *x, const float *signs, bool query_side,
+                                      uint8_t *codes, float *descale, int64_t heads,
+                                      int32_t n_seg, int64_t seg, int d, hipStream_t st);
 hipError_t launch_state_init(float *O_acc, float *m, float *l, int64_t rows, int d,
                              hipStream_t st);
 

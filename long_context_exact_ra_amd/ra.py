@@ -82,6 +82,8 @@ def load():
                                                      vp, vp]),
         "ra_fp8_tiles": (i64, [i64]),
         "ra_quantize_fp8": (ctypes.c_int, [i32, i32, i32, i32, i64, i32, vp, vp, vp, vp]),
+        "ra_quantize_fp8_hadamard": (ctypes.c_int, [i32, i32, i32, i64, i32, vp, vp, i32, vp,
+                                                    vp, vp]),
         "ra_share_forward_fp8": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, vp, vp, vp,
                                                 vp, vp, vp, f32, vp, vp, vp, vp, vp]),
         "ra_causal_share_forward_fp8": (ctypes.c_int, [i32, i32, i64, i32, i32, i32, i32, i32,
@@ -103,7 +105,8 @@ def exported_symbols() -> list[str]:
             "ra_finalize", "ra_share_forward", "ra_causal_share_forward", "ra_causal_pairs",
             "ra_share_backward", "ra_causal_share_backward", "ra_share_backward_workspace",
             "ra_share_backward_noalloc",
-            "ra_fp8_tiles", "ra_quantize_fp8", "ra_share_forward_fp8",
+            "ra_fp8_tiles", "ra_quantize_fp8", "ra_quantize_fp8_hadamard",
+            "ra_share_forward_fp8",
             "ra_causal_share_forward_fp8", "ra_strerror",
             "ra_last_hip_error"]
 
@@ -404,6 +407,27 @@ def quantize_fp8(kind, x, n_seg: int, codes, descale, stream=None):
     _check(load().ra_quantize_fp8(int(k), B, Hx, n_seg, seg, d, _dev(x, "x"),
                                   _dev(codes, "codes"), _dev(descale, "descale"),
                                   _stream(stream)), "ra_quantize_fp8")
+
+
+def quantize_fp8_hadamard(x, signs, n_seg: int, codes, descale, query_side: bool,
+                          stream=None):
+    """Incoherent processing then rows-mode block quantization of bf16 x [B, Hx,
+    n_seg*seg, d] (see ra_quantize_fp8_hadamard in ra.h): signs is a float32 device
+    tensor [d]; query_side folds 1/d into the descales (quantize Q with True, K with
+    False, the same signs)."""
+    B, Hx, R, d = x.shape
+    if n_seg < 1 or R % n_seg != 0:
+        raise ValueError("rows must split evenly into n_seg segments")
+    seg = R // n_seg
+    T = fp8_tiles(seg)
+    _need_shape(x, (B, Hx, R, d), "x", torch.bfloat16)
+    _need_shape(signs, (d,), "signs", torch.float32)
+    _need_shape(codes, (B, Hx, R, d), "codes", torch.uint8)
+    _need_shape(descale, (B, Hx, n_seg, T), "descale", torch.float32)
+    _check(load().ra_quantize_fp8_hadamard(B, Hx, n_seg, seg, d, _dev(x, "x"),
+                                           _dev(signs, "signs"), int(bool(query_side)),
+                                           _dev(codes, "codes"), _dev(descale, "descale"),
+                                           _stream(stream)), "ra_quantize_fp8_hadamard")
 
 
 def share_forward_fp8(rank: int, N: int, L: int, H: int, H_kv: int, d: int, B: int, Q8, qs, K8,

@@ -153,6 +153,10 @@ static void device_entry_points(char *p) {
     for (int kind : {RA_FP8_ROWS, RA_FP8_VT})
         EXPECT_OK(ra_quantize_fp8(kind, 1, 4, 8, 256, 128, p, p, f, st), "quantize");
     EXPECT_INVAL(ra_quantize_fp8(2, 1, 4, 8, 256, 128, p, p, f, st), "quantize kind");
+    EXPECT_OK(ra_quantize_fp8_hadamard(1, 4, 8, 256, 128, p, f, 1, p, f, st), "hadamard");
+    EXPECT_INVAL(ra_quantize_fp8_hadamard(1, 4, 8, 256, 128, p, nullptr, 0, p, f, st),
+                 "hadamard null signs");
+    EXPECT_INVAL(ra_quantize_fp8_hadamard(1, 4, 8, 256, 96, p, f, 0, p, f, st), "hadamard d");
     EXPECT_INVAL(ra_quantize_fp8(RA_FP8_ROWS, 1, 4, 0, 256, 128, p, p, f, st), "quantize n_seg");
     EXPECT_INVAL(ra_quantize_fp8(RA_FP8_ROWS, 1, 4, 8, 256, 96, p, p, f, st), "quantize d");
     EXPECT_OK(ra_share_forward_fp8(3, 8, 8 * 256, 4, 2, 128, 1, p, f, p, f, p, f, 0.1f, f, f, f,

@@ -88,6 +88,13 @@ hipError_t launch_finalize(float *, const float *, int64_t rows, int d, int, voi
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_quant_rows_hadamard(const void *, const float *, bool, uint8_t *, float *,
+                                      int64_t heads, int32_t n_seg, int64_t seg, int d,
+                                      hipStream_t) {
+    require(heads > 0 && n_seg > 0 && seg > 0 && (d == 64 || d == 128), "quant hadamard");
+    ++g_launches;
+    return hipSuccess;
+}
 // Stand-in for the static scratch lookup: a host buffer that the stub launches never read.
 alignas(256) static unsigned char g_scratch_stub[256];
 hipError_t noalloc_scratch(void **ptr) {

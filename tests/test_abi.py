@@ -375,3 +375,15 @@ def test_backward_noalloc_rejects_before_device_work():
     assert call(H=16, H_kv=16, N=1, L=rows // 16 + 1) == ra.RA_ESCRATCH
     assert call(B=2, H=64, H_kv=8, N=8, L=8 * 16384) == ra.RA_ESCRATCH
     assert b"scratch" in lib.ra_strerror(ra.RA_ESCRATCH)
+
+
+def test_quantize_fp8_hadamard_rejects():
+    lib = ra.load()
+    f = ctypes.c_void_p(0x30000)
+    assert lib.ra_quantize_fp8_hadamard(1, 2, 1, 64, 96, P, f, 0, P, f, None) == ra.RA_EINVAL
+    assert lib.ra_quantize_fp8_hadamard(1, 2, 0, 64, 128, P, f, 0, P, f, None) == ra.RA_EINVAL
+    assert lib.ra_quantize_fp8_hadamard(0, 2, 1, 64, 128, P, f, 0, P, f, None) == ra.RA_EINVAL
+    assert lib.ra_quantize_fp8_hadamard(1, 2, 1, 64, 128, P, None, 1, P, f, None) == ra.RA_EINVAL
+    assert lib.ra_quantize_fp8_hadamard(1, 2, 1, 64, 128, P, f, 1, None, f, None) == ra.RA_EINVAL
+    assert lib.ra_quantize_fp8_hadamard(1, 2, 1, 0, 128, None, None, 1, None, None,
+                                        None) == ra.RA_OK
