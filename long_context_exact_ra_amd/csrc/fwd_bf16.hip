@@ -79,6 +79,16 @@ __device__ __forceinline__ int64_t ring_block(int32_t rank, int64_t t, int32_t n
     return j < 0 ? j + n : j;
 }
 
+// max(x, x in lane ^ 32) in every lane: swapping the upper half of one copy of x with
+// the lower half of another leaves (x_lo, x_lo) in one register and (x_hi, x_hi) in the
+// other, so their maximum is the both-halves maximum in every lane.
+__device__ __forceinline__ float both_halves_max(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+                 __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 // Value of x in lane (lane ^ 32), via the gfx950 half-swap.
 __device__ __forceinline__ float other_half(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
@@ -300,18 +310,21 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         const int sw = swz_k<D>(ln);
         return ln * D + 8 * (hf ^ (sw & 1)) + 16 * (sw >> 1);
     }();
-    auto laundered_kbase = [&] {
-        int kb = kbase;
-        asm volatile("" : "+v"(kb));  // derive the read offsets where used, not kept live
-        return kb;
-    };
+    // Byte offsets of the K fragment reads, one per 16-deep contraction, computed once and
+    // kept in registers (opaque to the compiler, so it does not re-derive them per tile).
+    uint32_t kob[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        kob[kk] = (uint32_t)(kbase ^ (16 * kk)) * 2u;
+        asm volatile("" : "+v"(kob[kk]));
+    }
     constexpr int KK_STAGE = NKK / NSTAGE;  // contractions per pipeline stage
     static_assert(KK_STAGE >= 1 && NKK % NSTAGE == 0, "stage split");
-    auto scores_stage = [&](const bf16 *kt, int kb, Scores &d, int stage) {
+    auto scores_stage = [&](const bf16 *kt, Scores &d, int stage) {
 #pragma unroll
         for (int u = 0; u < KK_STAGE; ++u) {
             const int kk = stage * KK_STAGE + u;
-            const bf16 *kp = kt + (kb ^ (16 * kk));
+            const bf16 *kp = (const bf16 *)((const char *)kt + kob[kk]);
 #pragma unroll
             for (int b = 0; b < NH; ++b) {
                 const bf16x8 kf = *(const bf16x8 *)(kp + 32 * b * D);
@@ -325,10 +338,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     };
     auto scores_full = [&](const bf16 *kt, Scores &d) {
         zero_scores(d);
-        const int kb = laundered_kbase();
 #pragma unroll
         for (int stage = 0; stage < NSTAGE; ++stage) {
-            scores_stage(kt, kb, d, stage);
+            scores_stage(kt, d, stage);
             __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
         }
     };
@@ -366,8 +378,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
                 ma = fmaxf(fmaxf(ma, d.h[b][i]), d.h[b][i + 2]);
                 mb = fmaxf(fmaxf(mb, d.h[b][i + 1]), d.h[b][i + 3]);
             }
-        const float mx = fmaxf(ma, mb);
-        return fmaxf(mx, other_half(mx));
+        return both_halves_max(fmaxf(ma, mb));
     };
 
     // Softmax numerators of a score set, packed into the PV operands.  Operand c4
@@ -402,12 +413,16 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         const int x = 2 * (g16 & 1) + ((i16 & 3) >> 1);
         return vrow * D + 32 * sq + 8 * x + 4 * (i16 & 1);
     }();
+    uint32_t vob[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        vob[dt] = (uint32_t)(vbase ^ (32 * dt)) * 2u;
+        asm volatile("" : "+v"(vob[dt]));
+    }
     auto pv_part = [&](const bf16 *vt, const bf16x8 *pb, int c4) {
-        int vb = vbase;
-        asm volatile("" : "+v"(vb));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const bf16 *vp = vt + (vb ^ (32 * dt)) + 16 * c4 * D;
+            const bf16 *vp = (const bf16 *)((const char *)vt + vob[dt]) + 16 * c4 * D;
             const bf16x4 lo = tr_read(vp);
             const bf16x4 hi = tr_read(vp + 8 * D);
             const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -455,6 +470,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();
 
     bf16x8 pp[NSTAGE];  // packed softmax numerators of the tile whose P V product is next
+    // Non-causal: row maximum of the score set the next iteration consumes, taken before
+    // masking.  A ragged tile's keys past the block end are copies of the block's last
+    // key, so the unmasked maximum equals the masked one.
+    float mx_next = -INFINITY;
     {
         scores_full(K0, sx);
         mask_scores(sx, cM);
@@ -465,7 +484,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int part = 0; part < NSTAGE; ++part) softmax_part(sx, pp, part);
         lsum += tsum;
-        if (n_tiles > 1) scores_full(K1, sy);
+        if (n_tiles > 1) {
+            scores_full(K1, sy);
+            if constexpr (!CAUSAL) mx_next = row_max(sy);
+        }
     }
     __syncthreads();  // every wave is done with K buffer 0
     if (n_tiles > 2) {
@@ -489,20 +511,24 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         mask_scores(cs, cM);
         cM.next(act_of, a.n_blocks);
         bool changed;
-        const float alpha = update_reference(row_max(cs), changed);
+        const float alpha = update_reference(CAUSAL ? row_max(cs) : mx_next, changed);
         zero_scores(ns);
-        const int kb = laundered_kbase();
 #pragma unroll
         for (int stage = 0; stage < NSTAGE; ++stage) {
-            scores_stage(kcur, kb, ns, stage);
+            scores_stage(kcur, ns, stage);
             pv_part(vcur, pp, stage);
             softmax_part(cs, pp, stage);  // P(j+1) replaces P(j) after its product
         }
         lsum += tsum;
-        // Keep the numerators of tile j+1 in this block.  Left alone, the compiler sinks
-        // them past the rescale branch into the next iteration's block, so every other
-        // block has all the exponentials and the others have none beside their products.
-        asm volatile("" ::"v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(lsum));
+        // Non-causal: the row maximum of tile j+2 here, before the barrier, so that the
+        // next iteration can start its exponentials while its first fragment reads land.
+        if constexpr (!CAUSAL) mx_next = row_max(ns);
+        // Keep the numerators of tile j+1 (and that maximum) in this block.  Left alone,
+        // the compiler sinks them past the rescale branch into the next iteration's block,
+        // so every other block has all the exponentials and the others have none beside
+        // their products.
+        asm volatile("" ::"v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(lsum),
+                     "v"(mx_next));
         if (changed) rescale_output(alpha);  // after the old-reference products
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
         __syncthreads();
@@ -514,7 +540,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         mask_scores(cs, cM);
         cM.next(act_of, a.n_blocks);
         bool changed;
-        const float alpha = update_reference(row_max(cs), changed);
+        const float alpha = update_reference(CAUSAL ? row_max(cs) : mx_next, changed);
 #pragma unroll
         for (int stage = 0; stage < NSTAGE; ++stage) {
             pv_part(vcur, pp, stage);
