@@ -370,6 +370,7 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
 constexpr int KW = 4;         // waves per dK/dV work-group (one per SIMD), 32 keys each
 constexpr int KBR = 32 * KW;  // key rows per work-group
 constexpr int QBC = 64;       // query rows per streamed Q / dO tile
+constexpr int kReadAhead = 3;  // dK/dV: fragment reads this many product steps ahead
 
 // Causal: key tile i of a (batch, kv head) in order of its first key's position (the
 // earliest keys are seen by the most queries, so they go first).  Zigzag lists the first
@@ -502,37 +503,40 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int tb_lo0 = tr_base<D>(lane, 0), tb_hi0 = tr_base<D>(lane, 1);
     const float c = a.scale_log2;
 
-    // S = Q K^T and dP = dO V^T of the tile in buffer `buf`: lane = key ln, 16 queries per
-    // 32-query block, element i of block qb = query 32 qb + 8 (i/4) + 4 hf + i%4.
-    auto scores = [&](auto buf, f32x16 *sc, f32x16 *dq) {
+    // S = Q K^T and dP = dO V^T of the 32-query half qb of the tile in buffer `buf`: lane =
+    // key ln, 16 queries per lane, element i = query 32 qb + 8 (i/4) + 4 hf + i%4.
+    // Fragment reads run kReadAhead steps ahead of their products (one wave per SIMD:
+    // nothing else hides their latency).  The fences keep the
+    // reads and the products in this order and let vector and scalar work move across.
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0x0406); };
+    auto scores_half = [&](auto buf, int qb, f32x16 &sc, f32x16 &dq) {
         const bf16 *qt = Qt(buf), *ot = Ot(buf);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            sc[qb] = f32x16{};
-            dq[qb] = f32x16{};
-        }
+        sc = f32x16{};
+        dq = f32x16{};
         int kb = rb;
         asm volatile("" : "+v"(kb));
+        bf16x8 qa[NKK], oa[NKK];
+        auto rd = [&](int kk) {
+            const int off = (kb ^ (16 * kk)) + 32 * qb * D;
+            qa[kk] = *(const bf16x8 *)(qt + off);
+            oa[kk] = *(const bf16x8 *)(ot + off);
+        };
+        fence();
+#pragma unroll
+        for (int kk = 0; kk < kReadAhead; ++kk) rd(kk);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int off = (kb ^ (16 * kk)) + 32 * qb * D;
-                const bf16x8 qa = *(const bf16x8 *)(qt + off);
-                const bf16x8 oa = *(const bf16x8 *)(ot + off);
-                sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sc[qb], 0, 0, 0);
-                dq[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dq[qb], 0, 0, 0);
-            }
+            fence();
+            if (kk + kReadAhead < NKK) rd(kk + kReadAhead);
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], sc, 0, 0, 0);
+            dq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk], vf[kk], dq, 0, 0, 0);
         }
+        fence();
     };
-    // P and dS of tile t: rows past the end of the block get P = 0 and, with MK == 2
-    // (causal), so do queries before this lane's first query fq.  Packed in the contraction
-    // order of the gradient products (operand c4: queries 16 c4 + 8 (j/4) + 4 hf + j%4 =
-    // elements 8 (c4%2) + j of block c4/2).
     // Excluded pairs (rows past the end of the block; causal, queries before this lane's
     // first query fq) get score -inf, so P = 0 and dS = 0.  Only tiles that have any are
     // touched, behind a wave-uniform branch kept real by an empty volatile asm.
-    auto mask_tile = [&](int32_t t, f32x16 *sc) {
+    auto mask_half = [&](int32_t t, int qb, f32x16 &sc) {
         int32_t hh;
         const int32_t s_idx = tile_of(t, hh);
         const bool ragged = (int64_t)(s_idx + 1) * QBC > a.l_q;
@@ -542,97 +546,107 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int qlim = (left < QBC ? (int)left : QBC) - 4 * hf;  // valid query rows
         const int qthr = CAUSAL ? fq - s_idx * QBC - 4 * hf : -QBC;  // first seeing query
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int q = 32 * qb + 8 * (i >> 2) + (i & 3);  // query minus 4 hf
-                if (q >= qlim || q < qthr) sc[qb][i] = -INFINITY;
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int q = 32 * qb + 8 * (i >> 2) + (i & 3);  // query minus 4 hf
+            if (q >= qlim || q < qthr) sc[i] = -INFINITY;
+        }
     };
-    auto softmax = [&](auto buf, const f32x16 *sc, const f32x16 *dq, bf16x8 *pp, bf16x8 *dsp) {
+    // P and dS of one half, packed in the contraction order of the gradient products:
+    // operand h2 (c4 = 2 qb + h2) holds queries 16 c4 + 8 (j/4) + 4 hf + j%4, elements
+    // 8 h2 + j of the half's score block.
+    auto softmax_half = [&](auto buf, int qb, const f32x16 &sc, const f32x16 &dq, bf16x8 *pp,
+                            bf16x8 *dsp) {
         int wo = 4 * hf;
         asm volatile("" : "+v"(wo));
         const f32x2 *w = Wt(buf) + wo;
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int j4 = 0; j4 < 2; ++j4) {
                 // queries q0 .. q0 + 3, q0 = 16 c4 + 8 j4 + 4 hf: two 16-byte LDS reads
-                const int q0 = 16 * c4 + 8 * j4;  // minus 4 hf
+                const int q0 = 32 * qb + 16 * h2 + 8 * j4;  // minus 4 hf
                 const f32x4 w01 = *(const f32x4 *)(w + q0);
                 const f32x4 w23 = *(const f32x4 *)(w + q0 + 2);
                 const float Dq[4] = {w01[0], w01[2], w23[0], w23[2]};
                 const float Lq[4] = {w01[1], w01[3], w23[1], w23[3]};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * j4 + e, i = 8 * (c4 & 1) + j;
-                    const float p =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c4 >> 1][i], c, -Lq[e]));
-                    pp[c4][j] = (bf16)p;
-                    dsp[c4][j] = (bf16)(p * (dq[c4 >> 1][i] - Dq[e]));
+                    const int j = 4 * j4 + e, i = 8 * h2 + j;
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, -Lq[e]));
+                    pp[h2][j] = (bf16)p;
+                    dsp[h2][j] = (bf16)(p * (dq[i] - Dq[e]));
                 }
             }
     };
-    // dV^T += dO^T P and dK^T += Q^T dS: A = transposed reads of the dO / Q tiles.
-    auto grads = [&](auto buf, const bf16x8 *pp, const bf16x8 *dsp) {
+    // dV^T += dO^T P and dK^T += Q^T dS over one half: A = transposed reads of the dO / Q
+    // tiles.
+    auto grads_half = [&](auto buf, int qb, const bf16x8 *pp, const bf16x8 *dsp) {
         const bf16 *qt = Qt(buf), *ot = Ot(buf);
         int tb_lo = tb_lo0, tb_hi = tb_hi0;  // derived where used, not kept live per buffer
         asm volatile("" : "+v"(tb_lo), "+v"(tb_hi));
+        constexpr int NS = 2 * NDT;  // steps (h2, dt)
+        bf16x8 oa[NS], qa[NS];
+        auto rd = [&](int st) {
+            const int h2 = st / NDT, dt = st % NDT, c4 = 2 * qb + h2;
+            const int olo = (tb_lo ^ (32 * dt)) + 16 * c4 * D;
+            const int ohi = (tb_hi ^ (32 * dt)) + 16 * c4 * D;
+            const bf16x4 a0 = tr_read(ot + olo), a1 = tr_read(ot + ohi);
+            const bf16x4 b0 = tr_read(qt + olo), b1 = tr_read(qt + ohi);
+            oa[st] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            qa[st] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        };
+        fence();
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4)
+        for (int st = 0; st < kReadAhead; ++st) rd(st);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const int olo = (tb_lo ^ (32 * dt)) + 16 * c4 * D;
-                const int ohi = (tb_hi ^ (32 * dt)) + 16 * c4 * D;
-                const bf16x4 a0 = tr_read(ot + olo), a1 = tr_read(ot + ohi);
-                const bf16x4 b0 = tr_read(qt + olo), b1 = tr_read(qt + ohi);
-                const bf16x8 oa = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                const bf16x8 qa = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pp[c4], dv[dt], 0, 0, 0);
-                dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsp[c4], dk[dt], 0, 0, 0);
-            }
+        for (int st = 0; st < NS; ++st) {
+            fence();
+            if (st + kReadAhead < NS) rd(st + kReadAhead);
+            const int h2 = st / NDT, dt = st % NDT;
+            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[st], pp[h2], dv[dt], 0, 0, 0);
+            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], dsp[h2], dk[dt], 0, 0, 0);
+        }
+        fence();
     };
 
-    // Pipeline: iteration t runs the exponentials of tile t beside the score products of
-    // tile t+1, then tile t's gradient products; tile t+2 loads meanwhile.
+    // Pipeline over 32-query halves h of the 64-query tiles: the exponentials of half h
+    // run beside the score products of half h+1, then half h's gradient products.  One
+    // score set per half of a tile (s0: first half, s1: second half), so the products of
+    // the next half never overwrite what the exponentials still read.  Tile t+2 loads
+    // during tile t; one barrier per tile.
     load(0, IC<0>{});
     if (n_tiles > 1) load(1, IC<1>{});
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    // Two score sets alternate (unrolled by two), so the products of tile t+1 never
-    // overwrite registers the exponentials of tile t still read: no copies between
-    // iterations.
-    f32x16 sA[2], dA[2], sB[2], dB[2];
-    scores(IC<0>{}, sA, dA);
-    // Tile t in buffer t % 3, fixed at compile time (the loop is unrolled by six: three
-    // buffers times two score sets).
-    auto iteration = [&](auto buf, int32_t t, f32x16 *sc, const f32x16 *dc, f32x16 *sn,
-                         f32x16 *dn) {
+    f32x16 s0, d0, s1, d1;
+    scores_half(IC<0>{}, 0, s0, d0);
+    // Tile t in buffer t % 3, fixed at compile time (the loop is unrolled by three).
+    auto iteration = [&](auto buf, int32_t t) {
         constexpr int b = decltype(buf)::value;
         const IC<(b + 1) % 3> nb;   // tile t + 1
         const IC<(b + 2) % 3> nnb;  // tile t + 2 (held tile t - 1)
         if (t + 2 < n_tiles) load(t + 2, nnb);
-        bf16x8 pp[4], dsp[4];
-        mask_tile(t, sc);
-        softmax(buf, sc, dc, pp, dsp);
-        if (t + 1 < n_tiles) scores(nb, sn, dn);
-        grads(buf, pp, dsp);
+        bf16x8 pp0[2], dsp0[2], pp1[2], dsp1[2];
+        mask_half(t, 0, s0);
+        softmax_half(buf, 0, s0, d0, pp0, dsp0);
+        scores_half(buf, 1, s1, d1);
+        grads_half(buf, 0, pp0, dsp0);
+        mask_half(t, 1, s1);
+        softmax_half(buf, 1, s1, d1, pp1, dsp1);
+        // Unconditional, so these products share a block with the exponentials; after
+        // the last tile they read a stale (in-bounds) buffer and are never used.
+        scores_half(nb, 0, s0, d0);
+        grads_half(buf, 1, pp1, dsp1);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // tile t + 2 landed (this wave's part)
         __syncthreads();                     // everyone's part; tile t fully read
     };
-    for (int32_t t = 0;; t += 6) {
-        iteration(IC<0>{}, t, sA, dA, sB, dB);
+    for (int32_t t = 0;; t += 3) {
+        iteration(IC<0>{}, t);
         if (t + 1 >= n_tiles) break;
-        iteration(IC<1>{}, t + 1, sB, dB, sA, dA);
+        iteration(IC<1>{}, t + 1);
         if (t + 2 >= n_tiles) break;
-        iteration(IC<2>{}, t + 2, sA, dA, sB, dB);
+        iteration(IC<2>{}, t + 2);
         if (t + 3 >= n_tiles) break;
-        iteration(IC<0>{}, t + 3, sB, dB, sA, dA);
-        if (t + 4 >= n_tiles) break;
-        iteration(IC<1>{}, t + 4, sA, dA, sB, dB);
-        if (t + 5 >= n_tiles) break;
-        iteration(IC<2>{}, t + 5, sB, dB, sA, dA);
-        if (t + 6 >= n_tiles) break;
     }
 
     if (!kvalid) return;
