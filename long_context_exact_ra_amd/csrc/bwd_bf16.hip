@@ -27,6 +27,11 @@
 //    elementwise P / dS work is in-lane, and the bf16-packed P and dS are directly the B
 //    operands of the gradient products (the key / query order inside each 16-deep
 //    contraction is permuted to match, as in the forward kernel).
+//  * dK/dV splits each 32-key group between two waves of one SIMD: a producer (K, V
+//    resident; score products and exponentials) and a consumer (dK, dV accumulators;
+//    gradient products), with P and dS handed over through LDS once per query tile.
+//    Each wave then fits in half the register file, and the SIMD holds a wave of matrix
+//    products beside a wave of vector work.
 //
 // Causal shares (one K/V block per ring member, token positions from the layout): the
 // dQ kernel walks only the key tiles of each block that some query of its tile may
@@ -367,9 +372,10 @@ __global__ __launch_bounds__(64 * QW) void bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dK, dV
 
-constexpr int KW = 4;         // waves per dK/dV work-group (one per SIMD), 32 keys each
-constexpr int KBR = 32 * KW;  // key rows per work-group
-constexpr int QBC = 64;       // query rows per streamed Q / dO tile
+constexpr int KW = 4;          // key groups per dK/dV work-group, 32 keys each
+constexpr int KBR = 32 * KW;   // key rows per work-group
+constexpr int QBC = 64;        // query rows per streamed Q / dO tile
+constexpr int KWAVES = 2 * KW; // dK/dV waves: producers 0 .. KW-1, consumers KW .. 2 KW-1
 constexpr int kReadAhead = 3;  // dK/dV: fragment reads this many product steps ahead
 
 // Causal: key tile i of a (batch, kv head) in order of its first key's position (the
@@ -396,13 +402,18 @@ __device__ __forceinline__ void key_tile_of(int32_t i, int32_t layout, int32_t N
     }
 }
 
+// The dK/dV work of a key group is split between two waves on one SIMD.  The producer
+// holds the group's K and V rows and turns each query tile into P and dS (score
+// products, exponentials); the consumer holds the dK and dV accumulators and runs the
+// gradient products.  P and dS pass through LDS, one tile per barrier pair: while the
+// consumer works on tile t the producer computes tile t+1, so the SIMD has a wave of
+// matrix products beside the wave of vector work.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * KWAVES) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int NKK = D / 16, NDT = D / 32, TILE = QBC * D;
-    using TL = TileLoad<D, QBC, KW>;
-    // Three tile buffers: tile t is read by the gradient products while tile t+1 is read
-    // by the score products and tile t+2 is being loaded.
+    using TL = TileLoad<D, QBC, KWAVES>;
+    // Three Q / dO tile buffers: tile t is read by the gradient products while tile t+1 is
+    // read by the score products and tile t+2 is being loaded.
     __shared__ __attribute__((aligned(1024))) bf16 Qt0[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 Qt1[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 Qt2[TILE];
@@ -412,12 +423,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) f32x2 Wt0[QBC];    // (D, lse2) of the rows
     __shared__ __attribute__((aligned(16))) f32x2 Wt1[QBC];
     __shared__ __attribute__((aligned(16))) f32x2 Wt2[QBC];
+    // P and dS of one tile: per key group 8 operands (P, then dS, for c4 = 0..3) of 16
+    // bytes per lane, lane-contiguous.
+    __shared__ __attribute__((aligned(1024))) bf16x8 Xs[KW * 8 * 64];
     auto Qt = [&](auto b) { return pick<decltype(b)::value>(Qt0, Qt1, Qt2); };
     auto Ot = [&](auto b) { return pick<decltype(b)::value>(Ot0, Ot1, Ot2); };
     auto Wt = [&](auto b) { return pick<decltype(b)::value>(Wt0, Wt1, Wt2); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wave < KW;
+    const int kg = producer ? wave : wave - KW;  // key group (uniform)
     const int hf = lane >> 5, ln = lane & 31;
     const int wg = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, a.n_wg));
     const int kt_i = __builtin_amdgcn_readfirstlane(wg % a.n_ktiles);
@@ -431,28 +447,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
     j = __builtin_amdgcn_readfirstlane(j);
     u = __builtin_amdgcn_readfirstlane(u);
     const int32_t kblk = (int32_t)a.kblk_rows;
-    const int32_t bl = u * KBR + wave * 32 + ln;
+    const int32_t bl = u * KBR + kg * 32 + ln;
     const int64_t key = (int64_t)j * kblk + bl;  // this lane's key row
     const bool kvalid = bl < kblk;
     const int64_t kvoff = b * a.kv_batch_stride + g * a.kv_head_stride;
-
-    // Resident B operands: K and V rows of this lane's key.
-    bf16x8 kf[NKK], vf[NKK];
-    {
-        const int64_t off = kvoff + key * D + 8 * hf;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            kf[kk] = kvalid ? *(const bf16x8 *)((const bf16 *)a.K + off + 16 * kk) : bf16x8{};
-            vf[kk] = kvalid ? *(const bf16x8 *)((const bf16 *)a.V + off + 16 * kk) : bf16x8{};
-        }
-    }
-    f32x16 dk[NDT], dv[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        dk[dt] = f32x16{};
-        dv[dt] = f32x16{};
-        asm volatile("" : "+v"(dk[dt]), "+v"(dv[dt]));
-    }
 
     const int head_bytes = (int)(a.l_q * D * 2);
     const int32_t tiles_per_head = (int32_t)((a.l_q + QBC - 1) / QBC);
@@ -460,9 +458,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // hold all the queries that see a key of this work-group; fq is the first query that
     // sees this lane's key (positions grow with the local index in every layout).
     const CausalMap cmap{a.layout, a.rank, a.n_kblocks, kblk};
-    int32_t s_min = 0, fq = 0, fq_wave = 0;  // fq_wave: the largest fq of the wave
+    int32_t s_min = 0, fq = 0, fq_wave = 0;  // fq_wave: the largest fq of the key group
     if constexpr (CAUSAL) {
-        const int32_t last = kblk - 1, wlast = u * KBR + wave * 32 + 31;
+        const int32_t last = kblk - 1, wlast = u * KBR + kg * 32 + 31;
         s_min = __builtin_amdgcn_readfirstlane(cmap.first_query(cmap.pos(j, u * KBR)) / QBC);
         fq = cmap.first_query(cmap.pos(j, bl < last ? bl : last));
         fq_wave = __builtin_amdgcn_readfirstlane(
@@ -490,7 +488,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const uint32_t soff = (uint32_t)(r0 * D * 2);
         TL::run(qrs, soff, valid, Qt(buf), wave, lane);
         TL::run(ors, soff, valid, Ot(buf), wave, lane);
-        if (wave == KW - 1 && lane < QBC / 2) {  // 64 (D, lse2) pairs = 512 bytes
+        if (wave == KWAVES - 1 && lane < QBC / 2) {  // 64 (D, lse2) pairs = 512 bytes
             const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)((const f32x2 *)a.ws + bh * a.l_q), 0, (int)(a.l_q * 8), kRsrcWord3);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -498,96 +496,164 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 (int)(r0 * 8), 0, 0);
         }
     };
-
-    const int rb = row_base<D>(ln, hf);
-    const int tb_lo0 = tr_base<D>(lane, 0), tb_hi0 = tr_base<D>(lane, 1);
-    const float c = a.scale_log2;
-
-    // S = Q K^T and dP = dO V^T of the 32-query half qb of the tile in buffer `buf`: lane =
-    // key ln, 16 queries per lane, element i = query 32 qb + 8 (i/4) + 4 hf + i%4.
-    // Fragment reads run kReadAhead steps ahead of their products (one wave per SIMD:
-    // nothing else hides their latency).  The fences keep the
+    bf16x8 *xs = Xs + kg * 8 * 64 + lane;  // operand v of this lane at xs[64 v]
+    // Fragment reads run kReadAhead steps ahead of their products.  The fences keep the
     // reads and the products in this order and let vector and scalar work move across.
     auto fence = [] { __builtin_amdgcn_sched_barrier(0x0406); };
-    auto scores_half = [&](auto buf, int qb, f32x16 &sc, f32x16 &dq) {
-        const bf16 *qt = Qt(buf), *ot = Ot(buf);
-        sc = f32x16{};
-        dq = f32x16{};
-        int kb = rb;
-        asm volatile("" : "+v"(kb));
-        bf16x8 qa[NKK], oa[NKK];
-        auto rd = [&](int kk) {
-            const int off = (kb ^ (16 * kk)) + 32 * qb * D;
-            qa[kk] = *(const bf16x8 *)(qt + off);
-            oa[kk] = *(const bf16x8 *)(ot + off);
-        };
-        fence();
+
+    load(0, IC<0>{});
+    if (n_tiles > 1) load(1, IC<1>{});
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    if (producer) {
+        // Resident B operands: K and V rows of this lane's key.
+        bf16x8 kf[NKK], vf[NKK];
+        {
+            const int64_t off = kvoff + key * D + 8 * hf;
 #pragma unroll
-        for (int kk = 0; kk < kReadAhead; ++kk) rd(kk);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            fence();
-            if (kk + kReadAhead < NKK) rd(kk + kReadAhead);
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], sc, 0, 0, 0);
-            dq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk], vf[kk], dq, 0, 0, 0);
-        }
-        fence();
-    };
-    // Excluded pairs (rows past the end of the block; causal, queries before this lane's
-    // first query fq) get score -inf, so P = 0 and dS = 0.  Only tiles that have any are
-    // touched, behind a wave-uniform branch kept real by an empty volatile asm.
-    auto mask_half = [&](int32_t t, int qb, f32x16 &sc) {
-        int32_t hh;
-        const int32_t s_idx = tile_of(t, hh);
-        const bool ragged = (int64_t)(s_idx + 1) * QBC > a.l_q;
-        if (!(ragged || (CAUSAL && fq_wave > s_idx * QBC))) return;
-        asm volatile("" ::: "memory");
-        const int64_t left = a.l_q - (int64_t)s_idx * QBC;
-        const int qlim = (left < QBC ? (int)left : QBC) - 4 * hf;  // valid query rows
-        const int qthr = CAUSAL ? fq - s_idx * QBC - 4 * hf : -QBC;  // first seeing query
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int q = 32 * qb + 8 * (i >> 2) + (i & 3);  // query minus 4 hf
-            if (q >= qlim || q < qthr) sc[i] = -INFINITY;
-        }
-    };
-    // P and dS of one half, packed in the contraction order of the gradient products:
-    // operand h2 (c4 = 2 qb + h2) holds queries 16 c4 + 8 (j/4) + 4 hf + j%4, elements
-    // 8 h2 + j of the half's score block.
-    auto softmax_half = [&](auto buf, int qb, const f32x16 &sc, const f32x16 &dq, bf16x8 *pp,
-                            bf16x8 *dsp) {
-        int wo = 4 * hf;
-        asm volatile("" : "+v"(wo));
-        const f32x2 *w = Wt(buf) + wo;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int j4 = 0; j4 < 2; ++j4) {
-                // queries q0 .. q0 + 3, q0 = 16 c4 + 8 j4 + 4 hf: two 16-byte LDS reads
-                const int q0 = 32 * qb + 16 * h2 + 8 * j4;  // minus 4 hf
-                const f32x4 w01 = *(const f32x4 *)(w + q0);
-                const f32x4 w23 = *(const f32x4 *)(w + q0 + 2);
-                const float Dq[4] = {w01[0], w01[2], w23[0], w23[2]};
-                const float Lq[4] = {w01[1], w01[3], w23[1], w23[3]};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * j4 + e, i = 8 * h2 + j;
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, -Lq[e]));
-                    pp[h2][j] = (bf16)p;
-                    dsp[h2][j] = (bf16)(p * (dq[i] - Dq[e]));
-                }
+            for (int kk = 0; kk < NKK; ++kk) {
+                kf[kk] = kvalid ? *(const bf16x8 *)((const bf16 *)a.K + off + 16 * kk) : bf16x8{};
+                vf[kk] = kvalid ? *(const bf16x8 *)((const bf16 *)a.V + off + 16 * kk) : bf16x8{};
             }
-    };
-    // dV^T += dO^T P and dK^T += Q^T dS over one half: A = transposed reads of the dO / Q
-    // tiles.
-    auto grads_half = [&](auto buf, int qb, const bf16x8 *pp, const bf16x8 *dsp) {
+        }
+        const int rb = row_base<D>(ln, hf);
+        const float c = a.scale_log2;
+        // S = Q K^T and dP = dO V^T of the tile in buffer `buf`: lane = key ln, 16 queries
+        // per 32-query block, element i of block qb = query 32 qb + 8 (i/4) + 4 hf + i%4.
+        auto scores = [&](auto buf, f32x16 *sc, f32x16 *dq) {
+            const bf16 *qt = Qt(buf), *ot = Ot(buf);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                sc[qb] = f32x16{};
+                dq[qb] = f32x16{};
+            }
+            int kb = rb;
+            asm volatile("" : "+v"(kb));
+            constexpr int NS = 2 * NKK;  // steps (kk, qb)
+            bf16x8 qa[NS], oa[NS];
+            auto rd = [&](int st) {
+                const int kk = st / 2, qb = st % 2;
+                const int off = (kb ^ (16 * kk)) + 32 * qb * D;
+                qa[st] = *(const bf16x8 *)(qt + off);
+                oa[st] = *(const bf16x8 *)(ot + off);
+            };
+            fence();
+#pragma unroll
+            for (int st = 0; st < kReadAhead; ++st) rd(st);
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                fence();
+                if (st + kReadAhead < NS) rd(st + kReadAhead);
+                const int kk = st / 2, qb = st % 2;
+                sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kf[kk], sc[qb], 0, 0, 0);
+                dq[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[st], vf[kk], dq[qb], 0, 0, 0);
+            }
+            fence();
+        };
+        // Excluded pairs (rows past the end of the block; causal, queries before this
+        // lane's first query fq) get score -inf, so P = 0 and dS = 0.  Only tiles that
+        // have any are touched, behind a wave-uniform branch kept real by an empty
+        // volatile asm.
+        auto mask_tile = [&](int32_t t, f32x16 *sc) {
+            int32_t hh;
+            const int32_t s_idx = tile_of(t, hh);
+            const bool ragged = (int64_t)(s_idx + 1) * QBC > a.l_q;
+            if (!(ragged || (CAUSAL && fq_wave > s_idx * QBC))) return;
+            asm volatile("" ::: "memory");
+            const int64_t left = a.l_q - (int64_t)s_idx * QBC;
+            const int qlim = (left < QBC ? (int)left : QBC) - 4 * hf;  // valid query rows
+            const int qthr = CAUSAL ? fq - s_idx * QBC - 4 * hf : -QBC;  // first seeing query
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int q = 32 * qb + 8 * (i >> 2) + (i & 3);  // query minus 4 hf
+                    if (q >= qlim || q < qthr) sc[qb][i] = -INFINITY;
+                }
+        };
+        // P and dS, packed in the contraction order of the gradient products (operand c4:
+        // queries 16 c4 + 8 (j/4) + 4 hf + j%4 = elements 8 (c4%2) + j of block c4/2).
+        auto softmax = [&](auto buf, const f32x16 *sc, const f32x16 *dq, bf16x8 *pp,
+                           bf16x8 *dsp) {
+            int wo = 4 * hf;
+            asm volatile("" : "+v"(wo));
+            const f32x2 *w = Wt(buf) + wo;
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+                for (int j4 = 0; j4 < 2; ++j4) {
+                    // queries q0 .. q0 + 3, q0 = 16 c4 + 8 j4 + 4 hf: two 16-byte LDS reads
+                    const int q0 = 16 * c4 + 8 * j4;  // minus 4 hf
+                    const f32x4 w01 = *(const f32x4 *)(w + q0);
+                    const f32x4 w23 = *(const f32x4 *)(w + q0 + 2);
+                    const float Dq[4] = {w01[0], w01[2], w23[0], w23[2]};
+                    const float Lq[4] = {w01[1], w01[3], w23[1], w23[3]};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jj = 4 * j4 + e, i = 8 * (c4 & 1) + jj;
+                        const float p =
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c4 >> 1][i], c, -Lq[e]));
+                        pp[c4][jj] = (bf16)p;
+                        dsp[c4][jj] = (bf16)(p * (dq[c4 >> 1][i] - Dq[e]));
+                    }
+                }
+        };
+        f32x16 sc[2], dq[2];
+        bf16x8 pp[4], dsp[4];
+        scores(IC<0>{}, sc, dq);
+        mask_tile(0, sc);
+        softmax(IC<0>{}, sc, dq, pp, dsp);
+        // Iteration t (tile t in buffer t % 3, fixed at compile time: the loop is unrolled
+        // by three): publish P and dS of tile t, then compute those of tile t+1.
+        auto iteration = [&](auto buf, int32_t t) {
+            constexpr int bb = decltype(buf)::value;
+            const IC<(bb + 1) % 3> nb;   // tile t + 1
+            const IC<(bb + 2) % 3> nnb;  // tile t + 2 (held tile t - 1)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                xs[64 * v] = pp[v];
+                xs[64 * (4 + v)] = dsp[v];
+            }
+            __syncthreads();  // P and dS of tile t published
+            if (t + 2 < n_tiles) load(t + 2, nnb);
+            if (t + 1 < n_tiles) {
+                scores(nb, sc, dq);
+                mask_tile(t + 1, sc);
+                softmax(nb, sc, dq, pp, dsp);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // tile t + 2 landed (this wave's part)
+            __syncthreads();                     // everyone's part; tile t fully read
+        };
+        for (int32_t t = 0;; t += 3) {
+            iteration(IC<0>{}, t);
+            if (t + 1 >= n_tiles) break;
+            iteration(IC<1>{}, t + 1);
+            if (t + 2 >= n_tiles) break;
+            iteration(IC<2>{}, t + 2);
+            if (t + 3 >= n_tiles) break;
+        }
+        return;
+    }
+
+    // Consumer.
+    f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        dk[dt] = f32x16{};
+        dv[dt] = f32x16{};
+        asm volatile("" : "+v"(dk[dt]), "+v"(dv[dt]));
+    }
+    const int tb_lo0 = tr_base<D>(lane, 0), tb_hi0 = tr_base<D>(lane, 1);
+    // dV^T += dO^T P and dK^T += Q^T dS: A = transposed reads of the dO / Q tiles.
+    auto grads = [&](auto buf, const bf16x8 *pp, const bf16x8 *dsp) {
         const bf16 *qt = Qt(buf), *ot = Ot(buf);
         int tb_lo = tb_lo0, tb_hi = tb_hi0;  // derived where used, not kept live per buffer
         asm volatile("" : "+v"(tb_lo), "+v"(tb_hi));
-        constexpr int NS = 2 * NDT;  // steps (h2, dt)
+        constexpr int NS = 4 * NDT;  // steps (c4, dt)
         bf16x8 oa[NS], qa[NS];
         auto rd = [&](int st) {
-            const int h2 = st / NDT, dt = st % NDT, c4 = 2 * qb + h2;
+            const int c4 = st / NDT, dt = st % NDT;
             const int olo = (tb_lo ^ (32 * dt)) + 16 * c4 * D;
             const int ohi = (tb_hi ^ (32 * dt)) + 16 * c4 * D;
             const bf16x4 a0 = tr_read(ot + olo), a1 = tr_read(ot + ohi);
@@ -602,41 +668,24 @@ void bwd_dkdv_kernel(BwdArgs a) {
         for (int st = 0; st < NS; ++st) {
             fence();
             if (st + kReadAhead < NS) rd(st + kReadAhead);
-            const int h2 = st / NDT, dt = st % NDT;
-            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[st], pp[h2], dv[dt], 0, 0, 0);
-            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], dsp[h2], dk[dt], 0, 0, 0);
+            const int c4 = st / NDT, dt = st % NDT;
+            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[st], pp[c4], dv[dt], 0, 0, 0);
+            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], dsp[c4], dk[dt], 0, 0, 0);
         }
         fence();
     };
-
-    // Pipeline over 32-query halves h of the 64-query tiles: the exponentials of half h
-    // run beside the score products of half h+1, then half h's gradient products.  One
-    // score set per half of a tile (s0: first half, s1: second half), so the products of
-    // the next half never overwrite what the exponentials still read.  Tile t+2 loads
-    // during tile t; one barrier per tile.
-    load(0, IC<0>{});
-    if (n_tiles > 1) load(1, IC<1>{});
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    f32x16 s0, d0, s1, d1;
-    scores_half(IC<0>{}, 0, s0, d0);
-    // Tile t in buffer t % 3, fixed at compile time (the loop is unrolled by three).
     auto iteration = [&](auto buf, int32_t t) {
-        constexpr int b = decltype(buf)::value;
-        const IC<(b + 1) % 3> nb;   // tile t + 1
-        const IC<(b + 2) % 3> nnb;  // tile t + 2 (held tile t - 1)
+        constexpr int bb = decltype(buf)::value;
+        const IC<(bb + 2) % 3> nnb;  // tile t + 2 (held tile t - 1)
+        __syncthreads();  // P and dS of tile t published
         if (t + 2 < n_tiles) load(t + 2, nnb);
-        bf16x8 pp0[2], dsp0[2], pp1[2], dsp1[2];
-        mask_half(t, 0, s0);
-        softmax_half(buf, 0, s0, d0, pp0, dsp0);
-        scores_half(buf, 1, s1, d1);
-        grads_half(buf, 0, pp0, dsp0);
-        mask_half(t, 1, s1);
-        softmax_half(buf, 1, s1, d1, pp1, dsp1);
-        // Unconditional, so these products share a block with the exponentials; after
-        // the last tile they read a stale (in-bounds) buffer and are never used.
-        scores_half(nb, 0, s0, d0);
-        grads_half(buf, 1, pp1, dsp1);
+        bf16x8 pp[4], dsp[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            pp[v] = xs[64 * v];
+            dsp[v] = xs[64 * (4 + v)];
+        }
+        grads(buf, pp, dsp);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // tile t + 2 landed (this wave's part)
         __syncthreads();                     // everyone's part; tile t fully read
     };
@@ -683,7 +732,7 @@ hipError_t launch_all(const BwdArgs &a, const float *O, const void *dO, const fl
     if (e != hipSuccess) return e;
     BwdArgs k = a;
     k.n_wg = a.n_kv_wg;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(k.n_wg), dim3(64 * KW), 0, st, k);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(k.n_wg), dim3(64 * KWAVES), 0, st, k);
     return hipGetLastError();
 }
 

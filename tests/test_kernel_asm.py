@@ -110,14 +110,13 @@ def kernel_registers(asm):
 
 @pytest.mark.parametrize("src", HOT)
 def test_occupancy(src, assembly):
-    """Two waves per SIMD (an 8-wave work-group per CU) for the forward, FP8 and dQ kernels:
-    at most 256 registers per lane, VGPRs and AGPRs together. The dK/dV kernel runs one
-    wave per SIMD by design and may use all 512."""
+    """Two waves per SIMD (an 8-wave work-group per CU) for every kernel, the dK/dV
+    producer / consumer pairs included: at most 256 registers per lane, VGPRs and AGPRs
+    together."""
     regs = {k: v for k, v in kernel_registers(assembly(src)).items() if "prep" not in k}
     assert regs, "no kernels found in the metadata"
     for name, (vgpr, agpr) in regs.items():
-        limit = 512 if "dkdv" in name else 256
-        assert vgpr <= limit, f"{name}: {vgpr} registers (VGPR + AGPR), limit {limit}"
+        assert vgpr <= 256, f"{name}: {vgpr} registers (VGPR + AGPR), limit 256"
 
 
 # Kernels allowed to hold a private (scratch) segment, with the reason. The d = 128 FP8
