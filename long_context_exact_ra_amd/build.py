@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libra.so")
 SOURCES = ["ra_api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "util.hip", "bwd_bf16.hip",
            "fwd_fp8.hip", "fp8_quant.hip", "noalloc.hip"]
 ARCH = "gfx950"
-NO_NAN_SOURCES = {"fwd_bf16.hip"}
+NO_NAN_SOURCES = {"fwd_bf16.hip", "fwd_fp8.hip"}
 
 
 def hipcc() -> str:

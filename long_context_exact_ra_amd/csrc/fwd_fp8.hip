@@ -61,11 +61,14 @@ __device__ __forceinline__ int32_t ring_block(int32_t rank, int32_t t, int32_t n
     return j < 0 ? j + n : j;
 }
 
-__device__ __forceinline__ float other_half(float x) {
+// max(x, x in lane ^ 32) in every lane: swapping the upper half of one copy of x with
+// the lower half of another leaves (x_lo, x_lo) in one register and (x_hi, x_hi) in the
+// other, so their maximum is the both-halves maximum in every lane.
+__device__ __forceinline__ float both_halves_max(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const unsigned o = (threadIdx.x & 32) ? r[0] : r[1];
-    return __builtin_bit_cast(float, o);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+                 __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
             mb = fmaxf(fmaxf(mb, d.h[1][i]), d.h[1][i + 1]);
         }
         const float mx = fmaxf(ma, mb);
-        return fmaxf(mx, other_half(mx));
+        return both_halves_max(mx);
     };
     // Raise the reference when some row of the wave would exceed 2^kSlack; returns the
     // factor for the output and row sums accumulated under the old reference.
@@ -329,7 +332,9 @@ __global__ __launch_bounds__(NT) void fwd_fp8_kernel(Fp8Args a) {
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i0 + 1], ct, nR));
         const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i0 + 2], ct, nR));
         const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i0 + 3], ct, nR));
-        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        // Both halves of the word are written, so its previous contents (this operand's
+        // P of the tile before, already consumed) only name the register.
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb[q4], false);
         pb[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
     };
     auto rescale = [&](float alpha) {
