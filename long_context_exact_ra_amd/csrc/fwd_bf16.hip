@@ -344,10 +344,25 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
         }
     };
+    // Row max of a score set (raw dot units), both lane halves combined.
+    auto row_max = [&](const Scores &d) {
+        float ma = d.h[0][0], mb = d.h[0][1];
+#pragma unroll
+        for (int b = 0; b < NH; ++b)
+#pragma unroll
+            for (int i = (b == 0 ? 2 : 0); i < 16; i += 4) {
+                ma = fmaxf(fmaxf(ma, d.h[b][i]), d.h[b][i + 2]);
+                mb = fmaxf(fmaxf(mb, d.h[b][i + 1]), d.h[b][i + 3]);
+            }
+        return both_halves_max(fmaxf(ma, mb));
+    };
+
     // Keys past the end of a partial tile, and keys a causal share may not attend to,
     // get score -inf.
     const int32_t a_lane = qt * BR + qloc;  // this lane's local query index
-    auto mask_scores = [&](Scores &d, const TileCursor &cur) {
+    // mx holds the row maximum of d taken before masking; a tile that needs masking gets
+    // it taken again afterwards.
+    auto mask_scores = [&](Scores &d, const TileCursor &cur, float &mx) {
         const int64_t nvalid = a.blk_rows - (int64_t)cur.tin * BC;
         int keys = nvalid < BC ? (int)nvalid : BC;  // admissible prefix of the tile
         bool partial = keys < BC;
@@ -365,20 +380,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     if (32 * b + 8 * (i >> 2) + (i & 3) >= lim) d.h[b][i] = -INFINITY;
+            mx = row_max(d);
         }
-    };
-
-    // Row max of a score set (raw dot units), both lane halves combined.
-    auto row_max = [&](const Scores &d) {
-        float ma = d.h[0][0], mb = d.h[0][1];
-#pragma unroll
-        for (int b = 0; b < NH; ++b)
-#pragma unroll
-            for (int i = (b == 0 ? 2 : 0); i < 16; i += 4) {
-                ma = fmaxf(fmaxf(ma, d.h[b][i]), d.h[b][i + 2]);
-                mb = fmaxf(fmaxf(mb, d.h[b][i + 1]), d.h[b][i + 3]);
-            }
-        return both_halves_max(fmaxf(ma, mb));
     };
 
     // Softmax numerators of a score set, packed into the PV operands.  Operand c4
@@ -470,23 +473,23 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();
 
     bf16x8 pp[NSTAGE];  // packed softmax numerators of the tile whose P V product is next
-    // Non-causal: row maximum of the score set the next iteration consumes, taken before
-    // masking.  A ragged tile's keys past the block end are copies of the block's last
-    // key, so the unmasked maximum equals the masked one.
+    // Row maximum of the score set the next iteration consumes, taken before masking (the
+    // mask takes it again on the tiles that need one).
     float mx_next = -INFINITY;
     {
         scores_full(K0, sx);
-        mask_scores(sx, cM);
+        float mx0 = row_max(sx);
+        mask_scores(sx, cM, mx0);
         cM.next(act_of, a.n_blocks);
         bool changed;
-        const float alpha = update_reference(row_max(sx), changed);
+        const float alpha = update_reference(mx0, changed);
         if (changed) rescale_output(alpha);
 #pragma unroll
         for (int part = 0; part < NSTAGE; ++part) softmax_part(sx, pp, part);
         lsum += tsum;
         if (n_tiles > 1) {
             scores_full(K1, sy);
-            if constexpr (!CAUSAL) mx_next = row_max(sy);
+            mx_next = row_max(sy);
         }
     }
     __syncthreads();  // every wave is done with K buffer 0
@@ -508,10 +511,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
         }
         load_tile(vrs, cV, vnext, voff_g, true);
         cV.next(act_of, a.n_blocks);
-        mask_scores(cs, cM);
+        mask_scores(cs, cM, mx_next);
         cM.next(act_of, a.n_blocks);
         bool changed;
-        const float alpha = update_reference(CAUSAL ? row_max(cs) : mx_next, changed);
+        const float alpha = update_reference(mx_next, changed);
         zero_scores(ns);
 #pragma unroll
         for (int stage = 0; stage < NSTAGE; ++stage) {
@@ -520,9 +523,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             softmax_part(cs, pp, stage);  // P(j+1) replaces P(j) after its product
         }
         lsum += tsum;
-        // Non-causal: the row maximum of tile j+2 here, before the barrier, so that the
-        // next iteration can start its exponentials while its first fragment reads land.
-        if constexpr (!CAUSAL) mx_next = row_max(ns);
+        // The row maximum of tile j+2 here, before the barrier, so that the next iteration
+        // can start its exponentials while its first fragment reads land.
+        mx_next = row_max(ns);
         // Keep the numerators of tile j+1 (and that maximum) in this block.  Left alone,
         // the compiler sinks them past the rescale branch into the next iteration's block,
         // so every other block has all the exponentials and the others have none beside
@@ -537,10 +540,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     auto tail_iteration = [&](Scores &cs, const bf16 *vcur, bf16 *vnext) {
         load_tile(vrs, cV, vnext, voff_g, true);
         cV.next(act_of, a.n_blocks);
-        mask_scores(cs, cM);
+        mask_scores(cs, cM, mx_next);
         cM.next(act_of, a.n_blocks);
         bool changed;
-        const float alpha = update_reference(CAUSAL ? row_max(cs) : mx_next, changed);
+        const float alpha = update_reference(mx_next, changed);
 #pragma unroll
         for (int stage = 0; stage < NSTAGE; ++stage) {
             pv_part(vcur, pp, stage);
