@@ -130,7 +130,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-secondary", dest="secondary", action="store_false",
-                   help="skip the 32K share timed after the headline in the default run")
+                   help="skip the 32K share, FP8 and backward timings after the headline "
+                        "in the default run")
     p.add_argument("--no-step-path", dest="step_path", action="store_false",
                    help="skip the secondary timing of the per-step path "
                         "(N x ra_step + ra_finalize), which runs by default")
@@ -159,6 +160,37 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}))
 
 
+def _time_launches(step, steps: int, warmup: int):
+    """Warm-ups, then `steps` launches bracketed by HIP events on the launch stream:
+    (mean ms per step, sorted per-step ms)."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(stream)
+    for i in range(steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = marks[0].elapsed_time(marks[-1]) / steps
+    return ms, sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+
+
+def _secondary_record(name, kind, src, steps, ms, per_step, flops, peak, **more):
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {kind} {name}: {steps} steps, {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    return {"workload": name, "pass": kind, "steps": steps, "ms_per_step": round(ms, 4),
+            "step_ms": {"median": round(per_step[len(per_step) // 2], 4),
+                        "min": round(per_step[0], 4), "max": round(per_step[-1], 4)},
+            "value": round(tflops, 2), "unit": "TFLOP/s", "flops_per_step": flops, **more,
+            "kernel_source": os.path.basename(src), "kernel_sha": kernel_sha(src),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}}
+
+
 def time_secondary(name, args):
     """One more bf16 share timed with the headline's protocol; its own figures only."""
     import torch
@@ -176,28 +208,77 @@ def time_secondary(name, args):
         ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, q, k, v, scale, O)
 
     steps = max(args.steps, 100)  # a 32K share is 16x less work than the headline's
-    for _ in range(max(args.warmup, 10)):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    marks[0].record(stream)
-    for i in range(steps):
-        step()
-        marks[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms = marks[0].elapsed_time(marks[-1]) / steps
-    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
-    tflops = w.flops() / (ms * 1e-3) / 1e12
-    print(f"[bench] {name}: {steps} steps, {ms:.4f} ms/step", file=sys.stderr, flush=True)
-    return {"workload": name, "steps": steps, "ms_per_step": round(ms, 4),
-            "step_ms": {"median": round(per_step[len(per_step) // 2], 4),
-                        "min": round(per_step[0], 4), "max": round(per_step[-1], 4)},
-            "value": round(tflops, 2), "unit": "TFLOP/s",
-            "flops_per_step": w.flops(),
-            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}}
+    ms, per_step = _time_launches(step, steps, max(args.warmup, 10))
+    return _secondary_record(name, "forward", KERNEL_SRC, steps, ms, per_step, w.flops(),
+                             PEAK_BF16_TFLOPS)
+
+
+def time_secondary_fp8(name, args):
+    """The same share from E4M3 inputs (quantized once, before the timed launches)."""
+    import torch
+
+    from long_context_exact_ra_amd import ra, synth
+
+    w = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"[bench] drawing {name} (fp8)", file=sys.stderr, flush=True)
+    q, k, v = (x.to(dev) for x in synth.draw_workload(w))
+    scale = 1.0 / math.sqrt(w.d)
+    T = ra.fp8_tiles(w.l)
+    Q8 = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.uint8, device=dev)
+    qs = torch.empty((w.B, w.H, 1, T), dtype=torch.float32, device=dev)
+    K8 = torch.empty((w.B, w.H_kv, w.L, w.d), dtype=torch.uint8, device=dev)
+    ks = torch.empty((w.B, w.H_kv, w.N, T), dtype=torch.float32, device=dev)
+    V8 = torch.empty((w.B, w.H_kv, w.N, T, w.d, 64), dtype=torch.uint8, device=dev)
+    vs = torch.empty((w.B, w.H_kv, w.d), dtype=torch.float32, device=dev)
+    ra.quantize_fp8("rows", q, 1, Q8, qs)
+    ra.quantize_fp8("rows", k, w.N, K8, ks)
+    ra.quantize_fp8("vt", v, w.N, V8, vs)
+    del q, k, v
+    O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
+
+    def step():
+        ra.share_forward_fp8(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, Q8, qs, K8, ks, V8, vs,
+                             scale, O)
+
+    steps = max(args.steps, 20)
+    ms, per_step = _time_launches(step, steps, max(args.warmup, 3))
+    return _secondary_record(name, "forward, fp8 e4m3 products", os.path.join(CSRC, "fwd_fp8.hip"),
+                             steps, ms, per_step, w.flops(), PEAK_FP8_TFLOPS, dtype="fp8_e4m3")
+
+
+def time_secondary_backward(name, args):
+    """The share's backward (ra_share_backward) after one forward; algorithmic FLOP = 2.5x
+    the forward's (products S, dP, dV, dK, dQ)."""
+    import torch
+
+    from long_context_exact_ra_amd import ra, synth
+
+    w = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"[bench] drawing {name} (backward)", file=sys.stderr, flush=True)
+    q, k, v = (x.to(dev) for x in synth.draw_workload(w))
+    scale = 1.0 / math.sqrt(w.d)
+    g = torch.Generator().manual_seed(w.seed + 99)
+    dO = torch.randn((w.B, w.H, w.l, w.d), generator=g).to(torch.bfloat16).to(dev)
+    O = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
+    m = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
+    lo = torch.empty_like(m)
+    ra.share_forward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, q, k, v, scale, O, m, lo)
+    dQ = torch.empty_like(O)
+    dK = torch.zeros((w.B, w.H_kv, w.L, w.d), dtype=torch.float32, device=dev)
+    dV = torch.zeros_like(dK)
+    ws = torch.empty((max(16, int(ra.load().ra_share_backward_workspace(w.B, w.H, w.l))),),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        ra.share_backward(w.rank, w.N, w.L, w.H, w.H_kv, w.d, w.B, q, k, v, O, dO, m, lo,
+                          scale, dQ, dK, dV, ws)
+
+    steps = max(min(args.steps, 10), 5)
+    ms, per_step = _time_launches(step, steps, max(min(args.warmup, 3), 2))
+    return _secondary_record(name, "backward", os.path.join(CSRC, "bwd_bf16.hip"), steps, ms,
+                             per_step, 2.5 * w.flops(), PEAK_BF16_TFLOPS)
 
 
 def main():
@@ -422,12 +503,18 @@ def main():
         parity = {"rows": len(rows), "max_abs_err": float(err.max()),
                   "ok": bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ref)))}
 
-    # The other configuration the 50 % target names (the 32K share), timed the same way in
-    # the default run: warm-ups, HIP events on the launch stream, mean and median.
+    # The other configuration the 50 % target names (the 32K share), and the 128K share's FP8
+    # forward and bf16 backward, timed the same way in the default run: warm-ups, HIP events
+    # on the launch stream, mean and median.
     if (not args.workload or args.workload == synth.HEADLINE) and args.secondary and not (
             args.causal or args.backward or args.fp8):
         del qd, kd, vd, O
         extra["also"] = {"share_L32K_N8": time_secondary("share_L32K_N8", args)}
+        torch.cuda.empty_cache()
+        extra["also"]["fp8_share_L128K_N8"] = time_secondary_fp8("share_L128K_N8", args)
+        torch.cuda.empty_cache()
+        extra["also"]["backward_share_L128K_N8"] = time_secondary_backward("share_L128K_N8",
+                                                                           args)
 
     metric = "ring-share attention TFLOP/s (bf16) + % of MFMA peak at L=128K, N=8"
     if args.causal:
