@@ -359,6 +359,35 @@ def test_full_size_workload_sampled_rows(dev, name):
          f"{worst[1]:.3f}, lse err/bound {worst[2]:.3f}")
 
 
+def test_largest_head_range(dev):
+    """The largest key range one head may span: 2^23 - 1 keys of d = 128 bf16 are 2^31 - 256
+    bytes, the edge of the kernel's 32-bit buffer range (one key more is RA_ENOTSUP, checked
+    on the CPU).  N = 47 blocks of 178481 rows, so query tiles and key tiles are both ragged;
+    one head, rank 23; sampled rows (tile edges, both ends) against the oracle."""
+    B, H, H_kv, d, N, rank = 1, 1, 1, 128, 47, 23
+    L = (1 << 23) - 1
+    l = L // N
+    assert l * N == L and l % 64 != 0 and l % 256 != 0
+    _say("[largest head range] drawing inputs")
+    q, k, v = synth.draw(B, H, H_kv, d, l, L, "bf16", 1010)
+    scale = 1.0 / math.sqrt(d)
+    _say(f"[largest head range] running share rank {rank} of {N}, L = {L}")
+    O, m, lo, cast, trace = run_share(q.to(dev), k.to(dev), v.to(dev), rank, N, scale)
+    assert trace.cpu().tolist() == oracle.ring_schedule(rank, N)
+    assert torch.isfinite(O).all()
+    rows = sorted({0, 1, 255, 256, 12345, 65535, 65536, l // 2, l - 257, l - 256, l - 2, l - 1})
+    Q, K, V = host(q, k, v)
+    _say(f"[largest head range] oracle on {len(rows)} rows")
+    Or, M, Z = oracle.share(Q, K, V, scale, rank, N, rows=rows)
+    err = check_O(flat_rows(O, rows).cpu().numpy(), Or, "bf16", "largest head range")
+    check_O(flat_rows(cast, rows).float().cpu().numpy(), Or, "bf16", "largest head range cast")
+    bnd = stat_bounds_bf16(Q, K, (B, H, H_kv, d, l, L), scale, rows, M)
+    wm, wl = check_stats(flat_rows(m, rows).cpu().numpy(), flat_rows(lo, rows).cpu().numpy(), M,
+                         Z, "bf16", "largest head range", bounds=bnd)
+    _say(f"[largest head range] max abs err {err:.2e}, m err/bound {wm:.3f}, "
+         f"lse err/bound {wl:.3f}")
+
+
 def test_share_32k_every_row(dev):
     """The 32K share (4096 query rows of each of 32 heads against 32768 keys) against the
     oracle on every row, not a sample: O, its bf16 cast and the row statistics.  The
