@@ -144,6 +144,9 @@ def parse():
                    help="time every member's causal share under each layout (balance data)")
     p.add_argument("--fp8", action="store_true",
                    help="time the share from FP8 (e4m3) inputs (ra_share_forward_fp8) instead")
+    p.add_argument("--incoherent", action="store_true",
+                   help="with --fp8: quantize Q and K after a random-sign Hadamard rotation "
+                        "(ra_quantize_fp8_hadamard)")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -317,6 +320,8 @@ def main():
 
     if args.fp8 and args.backward:
         raise SystemExit("--fp8 times the forward share (optionally --causal) only")
+    if args.incoherent and not args.fp8:
+        raise SystemExit("--incoherent applies to --fp8 only")
     timed_src = os.path.join(
         CSRC, "fwd_fp8.hip" if args.fp8 else "bwd_bf16.hip" if args.backward else "fwd_bf16.hip")
     extra = {}
@@ -330,9 +335,18 @@ def main():
         V8 = torch.empty((w.B, w.H_kv, w.N, T, w.d, 64), dtype=u8, device=dev)
         vs = torch.empty((w.B, w.H_kv, w.d), dtype=f32, device=dev)
 
+        if args.incoherent:
+            gs = torch.Generator().manual_seed(w.seed + 21)
+            args.signs = torch.where(torch.rand(w.d, generator=gs) < 0.5, -1.0, 1.0).float()
+            signs_d = args.signs.to(dev)
+
         def quantize():
-            ra.quantize_fp8("rows", qd, 1, Q8, qs)
-            ra.quantize_fp8("rows", kd, w.N, K8, ks)
+            if args.incoherent:
+                ra.quantize_fp8_hadamard(qd, signs_d, 1, Q8, qs, query_side=True)
+                ra.quantize_fp8_hadamard(kd, signs_d, w.N, K8, ks, query_side=False)
+            else:
+                ra.quantize_fp8("rows", qd, 1, Q8, qs)
+                ra.quantize_fp8("rows", kd, w.N, K8, ks)
             ra.quantize_fp8("vt", vd, w.N, V8, vs)
 
         quantize()
@@ -546,7 +560,9 @@ def main():
                    "N": w.N, "rank": w.rank, "l": w.l, "flops_per_step": flops,
                    **({"causal": args.causal} if args.causal else {}),
                    **({"pass": "backward"} if args.backward else {}),
-                   **({"inputs": "fp8_e4m3, block-quantized"} if args.fp8 else {})},
+                   **({"inputs": "fp8_e4m3, block-quantized" + (
+                       " after a random-sign Hadamard rotation of Q and K"
+                       if args.incoherent else "")} if args.fp8 else {})},
         "pct_of_peak": round(100 * tflops / peak, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
@@ -607,8 +623,14 @@ def fp8_cpu_baseline(w, q, k, v, O, scale, args):
         g = h // group
         qh, kh, vh = (synth.to_oracle_array(x) for x in
                       (q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1]))
-        codes[h] = (*ofp8.quantize_rows(qh, 1, w.l), *ofp8.quantize_rows(kh, w.N, w.l),
-                    *ofp8.quantize_vt(vh, w.N, w.l))
+        if args.incoherent:
+            sg = args.signs.numpy()
+            codes[h] = (*ofp8.quantize_rows_hadamard(qh, sg, 1, w.l, True),
+                        *ofp8.quantize_rows_hadamard(kh, sg, w.N, w.l, False),
+                        *ofp8.quantize_vt(vh, w.N, w.l))
+        else:
+            codes[h] = (*ofp8.quantize_rows(qh, 1, w.l), *ofp8.quantize_rows(kh, w.N, w.l),
+                        *ofp8.quantize_vt(vh, w.N, w.l))
     threads = oracle.max_threads()
     def run_oracle(c, rows):
         if args.causal:
