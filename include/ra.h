@@ -33,6 +33,9 @@
  *  - With RA_BF16, one K (or V) head of the call, rows * d * 2 bytes, must stay
  *    below 2^31 bytes (the kernel addresses a head through a 32-bit buffer range);
  *    larger heads return RA_ENOTSUP.
+ *  - Sizes whose tensors or grids the kernels cannot address (a byte size beyond
+ *    int64, a grid beyond 2^31 - 1 work-groups) return RA_ENOTSUP; the checks
+ *    saturate rather than overflow, so no argument value makes them wrap round.
  */
 #ifndef RA_H
 #define RA_H
@@ -193,7 +196,8 @@ int ra_causal_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32
 /*
  * Number of (query, key) pairs member `rank`'s causal share evaluates per (batch,
  * head): the sum over its queries of the keys at or before each.  Host only; exact.
- * Returns -RA_EINVAL for bad N, rank, L (L % N != 0, L < 0) or layout (zigzag: odd l).
+ * Returns -RA_EINVAL for bad N, rank, L (L % N != 0, L < 0) or layout (zigzag: odd l),
+ * -RA_ENOTSUP if the count exceeds INT64_MAX.
  */
 int64_t ra_causal_pairs(int32_t rank, int32_t N, int64_t L, int32_t layout);
 
@@ -242,7 +246,8 @@ int ra_causal_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int3
                              float *dQ, float *dK, float *dV, void *workspace, void *stream);
 
 /* Bytes of workspace ra_share_backward (and ra_causal_share_backward) needs for B x H query rows of length l_q:
- * 8 * B * H * l_q (two floats per row).  Returns -RA_EINVAL for negative sizes. */
+ * 8 * B * H * l_q (two floats per row).  Returns -RA_EINVAL for negative sizes,
+ * -RA_ENOTSUP if the byte count does not fit int64. */
 int64_t ra_share_backward_workspace(int32_t B, int32_t H, int64_t l_q);
 
 /* Size of the static device scratch of ra_share_backward_noalloc: 8 MiB per GPU, enough

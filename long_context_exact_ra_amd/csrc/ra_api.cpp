@@ -60,6 +60,28 @@ int check_device() {
     return ok ? RA_OK : RA_ENOTSUP;
 }
 
+// Size arithmetic of the checks below, over non-negative operands.  A product that does
+// not fit int64 saturates at INT64_MAX, so an absurd size is rejected instead of wrapping
+// round (signed overflow), and a rounded-up quotient never forms a + b - 1.
+int64_t sat_mul(int64_t a, int64_t b) {
+    if (a == 0 || b == 0) return 0;
+    return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
+
+template <class... R>
+int64_t sat_mul(int64_t a, int64_t b, int64_t c, R... r) {
+    return sat_mul(sat_mul(a, b), c, (int64_t)r...);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+// True if a tensor of these extents, at up to 8 bytes an element, has a byte size (and so
+// every element and byte offset the kernels form) that fits int64.
+template <class... E>
+bool extent_ok(E... e) {
+    return sat_mul(8, (int64_t)e...) < INT64_MAX;
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool ptr_ok(const void *p) { return p != nullptr && aligned16(p); }
@@ -82,8 +104,8 @@ bool head_range_ok(int32_t dtype, int64_t rows, int32_t d) {
 bool grid_size(int32_t B, int32_t H, int64_t l_q, int32_t dtype, int32_t *n_qtiles,
                int32_t *n_wg) {
     const int64_t tile = dtype == RA_BF16 ? ra::bf16_query_tile() : ra::kF32QueryTile;
-    const int64_t qt = (l_q + tile - 1) / tile;
-    const int64_t total = qt * (int64_t)B * H;
+    const int64_t qt = ceil_div(l_q, tile);
+    const int64_t total = sat_mul(qt, B, H);
     if (qt > INT32_MAX || total > INT32_MAX) return false;
     *n_qtiles = (int32_t)qt;
     *n_wg = (int32_t)total;
@@ -109,7 +131,7 @@ int share_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, in
         !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast) ||
         (sched_trace != nullptr && ((uintptr_t)sched_trace & 3u) != 0))
         return RA_EINVAL;
-    if (!head_range_ok(dtype, L, d)) return RA_ENOTSUP;
+    if (!head_range_ok(dtype, L, d) || !extent_ok(B, H_kv, L, d)) return RA_ENOTSUP;
     const int64_t l = L / N;
     ra::FwdArgs a{};
     if (!grid_size(B, H, l, dtype, &a.n_qtiles, &a.n_wg)) return RA_ENOTSUP;
@@ -160,10 +182,10 @@ int backward_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv,
     const bool causal = layout != ra::kNoCausal;
     const int64_t kblk = causal ? lq : L;
     const int64_t nkb = causal ? N : 1;
-    const int64_t qt = (lq + ra::bwd_query_tile() - 1) / ra::bwd_query_tile();
-    const int64_t kpb = (kblk + ra::bwd_key_tile() - 1) / ra::bwd_key_tile();
+    const int64_t qt = ceil_div(lq, ra::bwd_query_tile());
+    const int64_t kpb = ceil_div(kblk, ra::bwd_key_tile());
     const int64_t kt = kpb * nkb;
-    if (qt * B * H > INT32_MAX || kt * B * H_kv > INT32_MAX) return RA_ENOTSUP;
+    if (sat_mul(qt, B, H) > INT32_MAX || sat_mul(kt, B, H_kv) > INT32_MAX) return RA_ENOTSUP;
     if (validate_only) return RA_OK;
     int rc = check_device();
     if (rc != RA_OK) return rc;
@@ -214,13 +236,13 @@ int fp8_share_launch(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv
         !opt_ptr_ok(l_out) || !opt_ptr_ok(O_cast))
         return RA_EINVAL;
     const int64_t l = L / N;
-    const int64_t T = (l + 63) / 64;
+    const int64_t T = ceil_div(l, 64);
     // one K head and one V head are each addressed through a 32-bit byte range
-    if (L * d > INT32_MAX || (int64_t)N * T * 64 * d > INT32_MAX ||
-        (int64_t)N * T * 4 > INT32_MAX)
+    if (sat_mul(L, d) > INT32_MAX || sat_mul(N, T, 64, d) > INT32_MAX ||
+        sat_mul(N, T, 4) > INT32_MAX)
         return RA_ENOTSUP;
-    const int64_t qt = (l + ra::fp8_query_tile() - 1) / ra::fp8_query_tile();
-    if (qt * B * H > INT32_MAX) return RA_ENOTSUP;
+    const int64_t qt = ceil_div(l, ra::fp8_query_tile());
+    if (sat_mul(qt, B, H) > INT32_MAX) return RA_ENOTSUP;
     int rc = check_device();
     if (rc != RA_OK) return rc;
     ra::Fp8Args a{};
@@ -274,6 +296,7 @@ int32_t ra_kv_head(int32_t h, int32_t H, int32_t H_kv) {
 int ra_state_init(float *O_acc, float *m, float *l, const ra_shape *s, void *stream) {
     if (s == nullptr || !heads_ok(s->B, s->H, s->H_kv, s->d, s->dtype) || s->l_q < 0)
         return RA_EINVAL;
+    if (!extent_ok(s->B, s->H, s->l_q, s->d)) return RA_ENOTSUP;
     const int64_t rows = (int64_t)s->B * s->H * s->l_q;
     if (rows == 0) return RA_OK;
     if (!ptr_ok(O_acc) || !ptr_ok(m) || !ptr_ok(l)) return RA_EINVAL;
@@ -288,11 +311,15 @@ int ra_step(const void *Q_i, const void *K_blk, const void *V_blk, float *O_acc,
     if (s == nullptr || !heads_ok(s->B, s->H, s->H_kv, s->d, s->dtype) || s->l_q < 0 ||
         s->l_kv < 0 || !scale_ok(scale) || s->kv_head_stride < 0 || s->kv_batch_stride < 0)
         return RA_EINVAL;
+    if (!extent_ok(s->l_kv, s->d)) return RA_ENOTSUP;
     const int64_t blk = s->l_kv * s->d;
     const int64_t hs = s->kv_head_stride ? s->kv_head_stride : blk;
+    if (hs < blk || hs % 8 != 0) return RA_EINVAL;
+    // H_kv heads at stride hs, then B batch entries at stride bs, must stay addressable
+    if (!extent_ok(s->H_kv, hs)) return RA_ENOTSUP;
     const int64_t bs = s->kv_batch_stride ? s->kv_batch_stride : (int64_t)s->H_kv * hs;
-    if (hs < blk || hs % 8 != 0 || bs % 8 != 0 || bs < (int64_t)(s->H_kv - 1) * hs + blk)
-        return RA_EINVAL;
+    if (bs % 8 != 0 || bs < (int64_t)(s->H_kv - 1) * hs + blk) return RA_EINVAL;
+    if (!extent_ok(s->B, bs) || !extent_ok(s->B, s->H, s->l_q, s->d)) return RA_ENOTSUP;
     if (s->l_q == 0 || s->l_kv == 0) return RA_OK;
     if (!ptr_ok(Q_i) || !ptr_ok(K_blk) || !ptr_ok(V_blk) || !ptr_ok(O_acc) || !ptr_ok(m) ||
         !ptr_ok(l))
@@ -326,6 +353,7 @@ int ra_step(const void *Q_i, const void *K_blk, const void *V_blk, float *O_acc,
 int ra_finalize(float *O_acc, const float *l, const ra_shape *s, void *O_out, void *stream) {
     if (s == nullptr || !heads_ok(s->B, s->H, s->H_kv, s->d, s->dtype) || s->l_q < 0)
         return RA_EINVAL;
+    if (!extent_ok(s->B, s->H, s->l_q, s->d)) return RA_ENOTSUP;
     const int64_t rows = (int64_t)s->B * s->H * s->l_q;
     if (rows == 0) return RA_OK;
     if (!ptr_ok(O_acc) || !ptr_ok(l) || !opt_ptr_ok(O_out)) return RA_EINVAL;
@@ -360,25 +388,31 @@ int ra_causal_share_forward(int32_t rank, int32_t N, int64_t L, int32_t H, int32
 
 int64_t ra_causal_pairs(int32_t rank, int32_t N, int64_t L, int32_t layout) {
     if (N < 1 || rank < 0 || rank >= N || L < 0 || L % N != 0) return -RA_EINVAL;
-    const int64_t l = L / N, r = rank;
+    // 128-bit arithmetic: every term below is at most L * l < 2^126, so none overflows.
+    const __int128 l = L / N, r = rank, n = N;
+    __int128 pairs;
     switch (layout) {
     case RA_LAYOUT_CONTIGUOUS:  // queries r*l + x see r*l + x + 1 keys
-        return l * r * l + l * (l + 1) / 2;
+        pairs = l * r * l + l * (l + 1) / 2;
+        break;
     case RA_LAYOUT_STRIPED:  // queries x*N + r see x*N + r + 1 keys
-        return (int64_t)N * (l * (l - 1) / 2) + l * (r + 1);
+        pairs = n * (l * (l - 1) / 2) + l * (r + 1);
+        break;
     case RA_LAYOUT_ZIGZAG: {  // chunk r then chunk 2N-1-r, h tokens each
         if (l % 2) return -RA_EINVAL;
-        const int64_t h = l / 2;
-        return h * (r * h) + h * (h + 1) / 2 + h * ((2 * (int64_t)N - 1 - r) * h) +
-               h * (h + 1) / 2;
+        const __int128 h = l / 2;
+        pairs = h * (r * h) + h * (h + 1) / 2 + h * ((2 * n - 1 - r) * h) + h * (h + 1) / 2;
+        break;
     }
     default: return -RA_EINVAL;
     }
+    return pairs > INT64_MAX ? -RA_ENOTSUP : (int64_t)pairs;
 }
 
 int64_t ra_share_backward_workspace(int32_t B, int32_t H, int64_t l_q) {
     if (B < 0 || H < 0 || l_q < 0) return -RA_EINVAL;
-    return 8 * (int64_t)B * H * l_q;
+    const int64_t bytes = sat_mul(8, B, H, l_q);  // a multiple of 8 unless saturated
+    return bytes == INT64_MAX ? -RA_ENOTSUP : bytes;
 }
 
 int ra_share_backward(int32_t rank, int32_t N, int64_t L, int32_t H, int32_t H_kv, int32_t d,
@@ -428,7 +462,7 @@ int ra_share_backward_noalloc(int32_t rank, int32_t N, int64_t L, int32_t H, int
 
 int64_t ra_fp8_tiles(int64_t seg) {
     if (seg < 0) return -RA_EINVAL;
-    return (seg + 63) / 64;
+    return ceil_div(seg, 64);
 }
 
 int ra_quantize_fp8(int32_t kind, int32_t B, int32_t Hx, int32_t n_seg, int64_t seg, int32_t d,
@@ -439,10 +473,10 @@ int ra_quantize_fp8(int32_t kind, int32_t B, int32_t Hx, int32_t n_seg, int64_t 
     if (seg == 0) return RA_OK;
     if (!ptr_ok(x) || !ptr_ok(codes) || !ptr_ok(descale)) return RA_EINVAL;
     const int64_t heads = (int64_t)B * Hx;
-    const int64_t T = (seg + 63) / 64;
-    const int64_t rows = (int64_t)n_seg * seg;
-    if (heads * n_seg * T > INT32_MAX || heads * ((rows + 255) / 256) > INT32_MAX ||
-        heads * d > INT32_MAX)
+    const int64_t T = ceil_div(seg, 64);
+    const int64_t rows = sat_mul(n_seg, seg);
+    if (sat_mul(heads, n_seg, T) > INT32_MAX || sat_mul(heads, ceil_div(rows, 256)) > INT32_MAX ||
+        sat_mul(heads, d) > INT32_MAX)
         return RA_ENOTSUP;
     int rc = check_device();
     if (rc != RA_OK) return rc;
@@ -461,8 +495,8 @@ int ra_quantize_fp8_hadamard(int32_t B, int32_t Hx, int32_t n_seg, int64_t seg, 
     if (seg == 0) return RA_OK;
     if (!ptr_ok(x) || !ptr_ok(signs) || !ptr_ok(codes) || !ptr_ok(descale)) return RA_EINVAL;
     const int64_t heads = (int64_t)B * Hx;
-    const int64_t T = (seg + 63) / 64;
-    if (heads * n_seg * T > INT32_MAX) return RA_ENOTSUP;
+    const int64_t T = ceil_div(seg, 64);
+    if (sat_mul(heads, n_seg, T) > INT32_MAX) return RA_ENOTSUP;
     int rc = check_device();
     if (rc != RA_OK) return rc;
     hipStream_t st = (hipStream_t)stream;

@@ -317,6 +317,8 @@ def _backward(rank, N, L, H, H_kv, d, B, layout, Q_i, K, V, O, dO, m, l, scale, 
     _need_shape(dK, (B, H_kv, L, d), "dK", torch.float32)
     _need_shape(dV, (B, H_kv, L, d), "dV", torch.float32)
     nbytes = int(load().ra_share_backward_workspace(B, H, lq))
+    if nbytes < 0:
+        raise RaError(-nbytes, "ra_share_backward_workspace")
     if workspace is None:
         workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=Q_i.device)
     elif workspace.numel() * workspace.element_size() < nbytes:

@@ -35,6 +35,13 @@ static int failures = 0;
         const int rc = (call);                                                \
         CHECK(rc == RA_EINVAL && g_launches == before, what);                 \
     } while (0)
+// Sizes beyond what the kernels address: RA_ENOTSUP, nothing launched.
+#define EXPECT_NOTSUP(call, what)                                             \
+    do {                                                                      \
+        const int before = g_launches;                                        \
+        const int rc = (call);                                                \
+        CHECK(rc == RA_ENOTSUP && g_launches == before, what);                \
+    } while (0)
 
 static void host_functions() {
     for (int N = 1; N <= 70; ++N)
@@ -167,10 +174,82 @@ static void device_entry_points(char *p) {
                                       f, p, st), "fp8 H % H_kv");
 }
 
+// Sizes whose products overflow 64 bits (the checks must saturate, not wrap): every call
+// returns RA_ENOTSUP without launching, and UBSan sees no signed overflow on the way.
+static void huge_sizes(char *p) {
+    float *f = (float *)p;
+    void *st = nullptr;
+    const int32_t big = std::numeric_limits<int32_t>::max();
+    const int64_t top = std::numeric_limits<int64_t>::max();
+    const int64_t top8 = top - top % 8;  // a multiple of N = 8
+
+    for (int dtype : {RA_F32, RA_BF16}) {
+        EXPECT_NOTSUP(ra_share_forward(0, 1, 1024, big, big, 128, big, dtype, p, p, p, 0.1f, f,
+                                       f, f, p, nullptr, st), "share: huge B, H");
+        EXPECT_NOTSUP(ra_causal_share_forward(0, 1, 1024, big, big, 64, big, dtype, 0, p, p, p,
+                                              0.1f, f, f, f, p, st), "causal: huge B, H");
+    }
+    EXPECT_NOTSUP(ra_share_forward(0, 1, top, 1, 1, 128, 1, RA_F32, p, p, p, 0.1f, f, f, f, p,
+                                   nullptr, st), "share f32: huge L");
+    EXPECT_NOTSUP(ra_share_forward(7, 8, top8, 1, 1, 128, 1, RA_F32, p, p, p, 0.1f, f, f, f, p,
+                                   nullptr, st), "share f32: huge L, N = 8");
+    EXPECT_NOTSUP(ra_share_forward(0, 1, (int64_t)1 << 40, 64, 64, 128, 1 << 20, RA_F32, p, p,
+                                   p, 0.1f, f, f, f, p, nullptr, st), "share f32: huge K/V");
+    EXPECT_NOTSUP(ra_share_backward(0, 1, 1024, big, big, 128, big, RA_BF16, p, p, p, f, p, f,
+                                    f, 0.1f, f, f, f, p, st), "backward: huge B, H");
+    EXPECT_NOTSUP(ra_causal_share_backward(0, 1, 1024, big, big, 128, big, RA_BF16, 1, p, p,
+                                           p, f, p, f, f, 0.1f, f, f, f, p, st),
+                  "causal backward: huge B, H");
+    EXPECT_NOTSUP(ra_share_backward_noalloc(0, 1, 1024, big, big, 128, big, RA_BF16, p, p, p,
+                                            f, p, f, f, 0.1f, f, f, f, st),
+                  "noalloc: huge B, H");
+    EXPECT_NOTSUP(ra_share_forward_fp8(0, 1, 1024, big, big, 128, big, p, f, p, f, p, f, 0.1f,
+                                       f, f, f, p, st), "fp8: huge B, H");
+    EXPECT_NOTSUP(ra_share_forward_fp8(0, 1, top, 1, 1, 128, 1, p, f, p, f, p, f, 0.1f, f, f,
+                                       f, p, st), "fp8: huge L");
+    EXPECT_NOTSUP(ra_share_forward_fp8(7, 8, top8, 1, 1, 128, 1, p, f, p, f, p, f, 0.1f, f, f,
+                                       f, p, st), "fp8: huge L, N = 8");
+    EXPECT_NOTSUP(ra_causal_share_forward_fp8(0, big - 1, (int64_t)(big - 1) * 64, 1, 1, 128,
+                                              1, 0, p, f, p, f, p, f, 0.1f, f, f, f, p, st),
+                  "causal fp8: huge N");
+
+    ra_shape s = {big, big, big, 128, top, top, 0, 0, RA_F32};
+    EXPECT_NOTSUP(ra_state_init(f, f, f, &s, st), "state init: huge rows");
+    EXPECT_NOTSUP(ra_finalize(f, f, &s, p, st), "finalize: huge rows");
+    EXPECT_NOTSUP(ra_step(p, p, p, f, f, f, 0.1f, &s, st), "step: huge sizes");
+    s = {1, 1, 1, 128, 64, top / 64, 0, 0, RA_F32};
+    EXPECT_NOTSUP(ra_step(p, p, p, f, f, f, 0.1f, &s, st), "step: huge key rows");
+    s = {1, 2, 2, 128, 64, 64, top - top % 8, 0, RA_F32};
+    EXPECT_NOTSUP(ra_step(p, p, p, f, f, f, 0.1f, &s, st), "step: huge head stride");
+    s = {big, 1, 1, 128, 64, 64, 64 * 128, top - top % 8, RA_F32};
+    EXPECT_NOTSUP(ra_step(p, p, p, f, f, f, 0.1f, &s, st), "step: huge batch stride");
+
+    for (int kind : {RA_FP8_ROWS, RA_FP8_VT}) {
+        EXPECT_NOTSUP(ra_quantize_fp8(kind, big, big, big, 256, 128, p, p, f, st),
+                      "quantize: huge B, Hx, n_seg");
+        EXPECT_NOTSUP(ra_quantize_fp8(kind, 1, 1, big, top, 128, p, p, f, st),
+                      "quantize: huge seg");
+    }
+    EXPECT_NOTSUP(ra_quantize_fp8_hadamard(big, big, big, 256, 128, p, f, 0, p, f, st),
+                  "hadamard: huge B, Hx, n_seg");
+    EXPECT_NOTSUP(ra_quantize_fp8_hadamard(1, 1, big, top, 64, p, f, 1, p, f, st),
+                  "hadamard: huge seg");
+
+    CHECK(ra_share_backward_workspace(big, big, top) == -RA_ENOTSUP, "workspace: overflow");
+    CHECK(ra_fp8_tiles(top) == top / 64 + 1, "fp8 tiles: largest seg");
+    for (int layout = 0; layout < 3; ++layout) {
+        CHECK(ra_causal_pairs(0, 2, top - top % 4, layout) == -RA_ENOTSUP,
+              "causal pairs: overflow");
+        CHECK(ra_causal_pairs(big - 1, big, (int64_t)big * 2, layout) > 0,
+              "causal pairs: many members");
+    }
+}
+
 int main() {
     host_functions();
     char *p = (char *)std::aligned_alloc(256, 4096);
     device_entry_points(p);
+    huge_sizes(p);
     std::free(p);
     if (failures) {
         std::fprintf(stderr, "%d failures\n", failures);

@@ -387,3 +387,38 @@ def test_quantize_fp8_hadamard_rejects():
     assert lib.ra_quantize_fp8_hadamard(1, 2, 1, 64, 128, P, f, 1, None, f, None) == ra.RA_EINVAL
     assert lib.ra_quantize_fp8_hadamard(1, 2, 1, 0, 128, None, None, 1, None, None,
                                         None) == ra.RA_OK
+
+
+# ------------------------------------------------------------------ sizes beyond 64 bits
+
+BIG = 2**31 - 1
+TOP = 2**63 - 1
+
+
+def test_sizes_beyond_64_bits_are_unsupported():
+    """Products of the size arguments that overflow int64 are rejected as unsupported,
+    not wrapped round into small (and so accepted) values."""
+    for dtype in (ra.RA_F32, ra.RA_BF16):
+        assert _share(rank=0, N=1, L=1024, B=BIG, H=BIG, H_kv=BIG, dtype=dtype) == ra.RA_ENOTSUP
+    assert _share(rank=7, N=8, L=TOP - TOP % 8, H=1, H_kv=1, dtype=ra.RA_F32) == ra.RA_ENOTSUP
+    for causal in (False, True):
+        assert _backward(causal, rank=0, N=1, L=1024, B=BIG, H=BIG, H_kv=BIG) == ra.RA_ENOTSUP
+    assert _fp8(rank=0, N=1, L=1024, B=BIG, H=BIG, H_kv=BIG) == ra.RA_ENOTSUP
+    assert _fp8(rank=7, N=8, L=TOP - TOP % 8, H=1, H_kv=1) == ra.RA_ENOTSUP
+    assert _quant(B=BIG, Hx=BIG, n_seg=BIG, seg=256) == ra.RA_ENOTSUP
+    assert _quant(B=1, Hx=1, n_seg=BIG, seg=TOP) == ra.RA_ENOTSUP
+    lib = ra.load()
+    assert lib.ra_share_backward_workspace(BIG, BIG, TOP) == -ra.RA_ENOTSUP
+    assert lib.ra_fp8_tiles(TOP) == TOP // 64 + 1
+    for layout in range(3):
+        assert lib.ra_causal_pairs(0, 2, TOP - TOP % 4, layout) == -ra.RA_ENOTSUP
+    # counts just below 2^63 stay exact: each query's key count rises by a fixed step
+    # along the share (contiguous 1, striped N), so the total is an arithmetic series,
+    # l * (first + last) / 2, taken here in Python's exact integers
+    N, L = 2, 2**32
+    l = L // N
+    for layout, first, step in ((0, l + 1, 1), (1, 2, N)):
+        last = first + (l - 1) * step
+        want = l * (first + last) // 2
+        assert 2**62 < want < 2**63
+        assert lib.ra_causal_pairs(1, N, L, layout) == want
