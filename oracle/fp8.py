@@ -213,18 +213,24 @@ def error_bounds(Qd, Kd, Vd, scale, rank: int, N: int, O_ref, rows, layout=None)
     bO = np.empty((len(rows), d))
     bm = np.empty(len(rows))
     bl = np.empty(len(rows))
+    held = (None, None, None)  # (batch, K/V head), |K|, |V| of the last row's head
     for i, r in enumerate(rows):
         b, h, q = r // (H * l), (r // l) % H, r % l
         k, v = Kd[b, h // g], Vd[b, h // g]
+        if held[0] != (b, h // g):  # |K| and |V| once per head, not once per row
+            held = ((b, h // g), np.abs(k), np.abs(v))
+        ak, av = held[1], held[2]
         if layout is not None:
             keep = kpos <= qpos[q]
-            k, v = k[keep], v[keep]
+            k, v, ak, av = k[keep], v[keep], ak[keep], av[keep]
         s = scale * (k @ Qd[b, h, q])
-        ds = 2.0 ** -10 * scale * (np.abs(k) @ np.abs(Qd[b, h, q]))
+        ds = 2.0 ** -10 * scale * (ak @ np.abs(Qd[b, h, q]))
         P = np.exp(s - s.max())
         Z = P.sum()
         e = np.maximum(2.0 ** -4 * P, 2.0 ** -14) + 1.1 * P * np.expm1(ds)
-        bO[i] = (2 * (e @ np.abs(v - O_ref[i])) + acc * (P @ np.abs(v))) / Z + 1e-6
+        dev = np.subtract(v, O_ref[i])
+        np.abs(dev, out=dev)
+        bO[i] = (2 * (e @ dev) + acc * (P @ av)) / Z + 1e-6
         bm[i] = ds.max() + 1e-6 * max(1.0, abs(s.max()))
         bl[i] = 2 * e.sum() + P @ np.expm1(ds + ds.max()) + acc * Z
     return bO, bm, bl

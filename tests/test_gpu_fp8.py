@@ -216,9 +216,13 @@ def test_fp8_share_every_rank(dev):
 @pytest.mark.parametrize("name", ["share_L32K_N8", "share_L128K_N8", "gqa_L128K_N8_28q4kv",
                                   "share_L1M_N64_std3"])
 def test_fp8_full_size_sampled_rows(dev, name):
-    """The bf16 workloads' shapes quantized and run on the GPU in one launch each; for two
-    heads the oracle quantizes the same bf16 inputs itself (codes compared bit for bit)
-    and evaluates sampled rows on both sides of query-tile boundaries."""
+    """The bf16 workloads' shapes quantized and run on the GPU in one launch each; for
+    sampled heads the oracle quantizes the same bf16 inputs itself (codes compared bit for
+    bit) and evaluates sampled rows of each: the first and last, both sides of the first
+    and last 256-row work-group boundary and of every `tile` boundary, topped up with
+    seeded rows.  Up to 128K keys: four heads spread over the K/V groups, 160 rows of the
+    32K share (every work-group boundary) and 68 of the 128K shares.  The 1M share, whose
+    oracle quantization of one head takes most of a minute: its last head, 16 rows."""
     w = synth.WORKLOADS[name]
     q, k, v = synth.draw_workload(w)
     scale = 1.0 / math.sqrt(w.d)
@@ -226,8 +230,15 @@ def test_fp8_full_size_sampled_rows(dev, name):
     (O, m, lo, Oc), gpu = run_fp8_share(q, k, v, w.N, w.rank, scale, dev, cast=True)
     Q8, qs, K8, ks, V8, vs = gpu
     group = w.H // w.H_kv
-    local = np.array([0, 63, 64, 255, 256, 1000, w.l // 2, w.l - 257, w.l - 1], np.int64)
-    heads = (w.H - 1,) if w.L > 131072 else (1, w.H - 1)  # one head of the 1M share
+    if w.L > 131072:
+        heads, n_rows, tile = (w.H - 1,), 12, 4096
+    elif w.l <= 4096:
+        heads, n_rows, tile = sorted({0, 1 % w.H, w.H // 2, w.H - 1}), 160, 256
+    else:
+        heads, n_rows, tile = sorted({0, 1 % w.H, w.H // 2, w.H - 1}), 64, 1024
+    local = set(synth.boundary_rows(1, 1, w.l, n_rows, w.seed, tile=tile))
+    local |= {255, 256, w.l - 257, w.l - 256}
+    local = np.array(sorted(local), np.int64)
     for h in heads:
         g = h // group
         _say(f"[fp8 {name}] oracle quantization and {len(local)} rows of head {h}")

@@ -89,6 +89,12 @@ def test_schedule_equals_message_passing_simulation(N):
 
 
 def test_kv_head_contiguous_groups():
+    # The grouping of grouped-query attention as torch applies it (each K/V head repeated
+    # for H / H_kv consecutive query heads, repeat_interleave), for every divisor pair.
+    for H in (1, 2, 6, 8, 28, 32, 64):
+        for H_kv in (g for g in range(1, H + 1) if H % g == 0):
+            want = torch.arange(H_kv).repeat_interleave(H // H_kv).tolist()
+            assert [oracle.kv_head(h, H, H_kv) for h in range(H)] == want, (H, H_kv)
     assert [oracle.kv_head(h, 28, 4) for h in range(28)] == [h // 7 for h in range(28)]
     assert [oracle.kv_head(h, 8, 8) for h in range(8)] == list(range(8))
     assert [oracle.kv_head(h, 8, 1) for h in range(8)] == [0] * 8
