@@ -220,9 +220,9 @@ def test_fp8_full_size_sampled_rows(dev, name):
     sampled heads the oracle quantizes the same bf16 inputs itself (codes compared bit for
     bit) and evaluates sampled rows of each: the first and last, both sides of the first
     and last 256-row work-group boundary and of every `tile` boundary, topped up with
-    seeded rows.  Up to 128K keys: four heads spread over the K/V groups, 160 rows of the
-    32K share (every work-group boundary) and 68 of the 128K shares.  The 1M share, whose
-    oracle quantization of one head takes most of a minute: its last head, 16 rows."""
+    seeded rows.  Up to 128K keys: four heads spread over the K/V groups, with every 256-row
+    work-group boundary (160 rows of the 32K share, 128 of the 128K shares).  The 1M share,
+    whose oracle quantization of one head is the slow part: its last head, 28 rows."""
     w = synth.WORKLOADS[name]
     q, k, v = synth.draw_workload(w)
     scale = 1.0 / math.sqrt(w.d)
@@ -231,11 +231,9 @@ def test_fp8_full_size_sampled_rows(dev, name):
     Q8, qs, K8, ks, V8, vs = gpu
     group = w.H // w.H_kv
     if w.L > 131072:
-        heads, n_rows, tile = (w.H - 1,), 12, 4096
-    elif w.l <= 4096:
-        heads, n_rows, tile = sorted({0, 1 % w.H, w.H // 2, w.H - 1}), 160, 256
+        heads, n_rows, tile = (w.H - 1,), 24, 4096
     else:
-        heads, n_rows, tile = sorted({0, 1 % w.H, w.H // 2, w.H - 1}), 64, 1024
+        heads, n_rows, tile = sorted({0, 1 % w.H, w.H // 2, w.H - 1}), 160 if w.l <= 4096 else 0, 256
     local = set(synth.boundary_rows(1, 1, w.l, n_rows, w.seed, tile=tile))
     local |= {255, 256, w.l - 257, w.l - 256}
     local = np.array(sorted(local), np.int64)
