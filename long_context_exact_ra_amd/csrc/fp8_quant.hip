@@ -178,40 +178,67 @@ __global__ void vt_finalize_kernel(float *descale, int64_t n) {
     if (i < n) descale[i] = descale_of(descale[i]);
 }
 
-// One stored tile per work-group: thread (channel c, row group rg) quantizes rows
-// 64u + RG*rg ... of channel c and writes them as RG consecutive bytes of row c of the
-// transposed tile.
+// One stored tile per work-group, transposed through LDS.  Load phase: each thread reads
+// RPT consecutive rows of 8 channels (16-byte loads; each row of the tile is read whole by
+// CPR neighbouring lanes), quantizes every value as in rows mode with its channel's scale
+// (rows past the segment's end are zero) and writes each channel's RPT codes as one word
+// of that channel's row in LDS (channel-major, row stride VS; VS / 4 odd spreads the rows
+// over the banks).  Store phase: thread (channel c, row group rg) copies the RG codes
+// RG*rg ... of channel row c to the stored tile.
 template <int D>
 __global__ __launch_bounds__(256) void vt_quant_kernel(const bf16 *x, uint8_t *codes,
                                                        const float *descale, int32_t n_seg,
                                                        int64_t seg, int32_t T) {
-    constexpr int NG = 256 / D;  // row groups
-    constexpr int RG = QT / NG;  // rows per thread: 32 (d = 128) or 16 (d = 64)
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int RPT = QT * CPR / 256;    // rows per thread in the load phase: 4 or 2
+    constexpr int NG = 256 / D;            // row groups of the store phase
+    constexpr int RG = QT / NG;            // codes per thread: 32 (d = 128) or 16 (d = 64)
+    constexpr int VS = QT + 4;             // LDS bytes per channel row
+    static_assert(RPT == 4 || RPT == 2, "load phase packs 2 or 4 rows per channel");
+    __shared__ __attribute__((aligned(16))) uint8_t tile[D * VS];
     const int64_t wg = blockIdx.x;
     const int u = (int)(wg % T);
     const int64_t hs = wg / T;
     const int s = (int)(hs % n_seg);
     const int64_t hd = hs / n_seg;
-    const int c = threadIdx.x % D, rg = threadIdx.x / D;
     const int64_t left = seg - (int64_t)u * QT;
     const int nrows = left < QT ? (int)left : QT;
-    const float inv = 1.0f / descale[hd * D + c];
-    const bf16 *xp = x + ((hd * n_seg + s) * seg + (int64_t)u * QT) * D + c;
-    unsigned w[RG / 4];
+    const bf16 *xt = x + ((hd * n_seg + s) * seg + (int64_t)u * QT) * D;
+    const int c8 = threadIdx.x % CPR, r0 = RPT * (threadIdx.x / CPR);
+    float inv[8];
 #pragma unroll
-    for (int k = 0; k < RG / 4; ++k) {
-        float f[4];
+    for (int e = 0; e < 8; ++e) inv[e] = 1.0f / descale[hd * D + 8 * c8 + e];
+    float f[RPT][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = RG * rg + 4 * k + e;
-            f[e] = r < nrows ? (float)xp[(int64_t)r * D] * inv : 0.f;
+    for (int k = 0; k < RPT; ++k) {
+        const int r = r0 + k;
+        if (r < nrows) {
+            const bf16x8 v = *(const bf16x8 *)(xt + (int64_t)r * D + 8 * c8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[k][e] = (float)v[e] * inv[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[k][e] = 0.f;
         }
-        w[k] = pack4(f[0], f[1], f[2], f[3]);
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint8_t *tp = tile + (8 * c8 + e) * VS + r0;
+        if constexpr (RPT == 4)
+            *(unsigned *)tp = pack4(f[0][e], f[1][e], f[2][e], f[3][e]);
+        else
+            *(uint16_t *)tp =
+                (uint16_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[0][e], f[1][e], 0, false);
+    }
+    __syncthreads();
+    const int c = threadIdx.x % D, rg = threadIdx.x / D;
+    const uint8_t *src = tile + c * VS + RG * rg;
     uint8_t *op = codes + (hs * T + u) * (int64_t)(D * QT) + c * QT + RG * rg;
 #pragma unroll
-    for (int k = 0; k < RG / 16; ++k)
-        *(u32x4 *)(op + 16 * k) = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+    for (int k = 0; k < RG / 16; ++k) {
+        const unsigned *sp = (const unsigned *)(src + 16 * k);
+        *(u32x4 *)(op + 16 * k) = u32x4{sp[0], sp[1], sp[2], sp[3]};
+    }
 }
 
 template <int D, bool ROT>
