@@ -145,12 +145,17 @@ def check(name, got, ref, mag):
     return float(worst)
 
 
-# (B, H, H_kv, d, N, l): ragged query and key counts, GQA, both head sizes, N = 1
+# (B, H, H_kv, d, N, l): ragged query and key counts, GQA, both head sizes, N = 1, and
+# sequences shorter than one 128-key work-group (one key; 40 and 99 keys, which leave whole
+# 32-key groups of the work-group without a key)
 CASES = [
     (1, 2, 1, 128, 2, 300),
     (2, 4, 2, 64, 3, 256),
     (1, 2, 2, 128, 1, 512),
     (1, 3, 3, 128, 4, 200),
+    (1, 1, 1, 64, 1, 1),
+    (1, 2, 1, 128, 2, 20),
+    (2, 2, 2, 128, 3, 33),
 ]
 
 

@@ -64,6 +64,7 @@ BF16_CASES = [
     (1, 3, 3, 128, 4, 300),   # ragged: not a multiple of 64 or 256 (no zigzag)
     (1, 2, 2, 128, 2, 1024),
     (1, 2, 2, 128, 1, 640),   # a single member: plain causal attention
+    (1, 2, 1, 128, 3, 5),     # blocks of 5 keys: one ragged tile per block (no zigzag)
 ]
 
 

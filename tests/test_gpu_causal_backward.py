@@ -88,7 +88,7 @@ def compare(q, k, v, do, N, rank, layout, scale, dev, tag):
 
 
 # (layout, B, H, H_kv, d, N, l): ragged blocks (contiguous / striped), zigzag half-blocks
-# of one and of several tiles, GQA, both head sizes
+# of one and of several tiles, GQA, both head sizes, and blocks shorter than one 32-key group
 CASES = [
     ("contiguous", 1, 2, 1, 128, 3, 300),
     ("contiguous", 2, 2, 2, 64, 2, 256),
@@ -96,6 +96,8 @@ CASES = [
     ("striped", 1, 2, 2, 128, 3, 384),
     ("zigzag", 1, 3, 3, 128, 2, 384),
     ("zigzag", 1, 4, 2, 64, 4, 256),
+    ("contiguous", 1, 2, 1, 128, 3, 7),
+    ("striped", 1, 1, 1, 64, 4, 1),
 ]
 
 

@@ -183,6 +183,7 @@ SHARE_CASES = [
     (1, 3, 3, 128, 1, 64),
     (1, 2, 2, 64, 5, 1000),
     (1, 1, 1, 128, 2, 33),
+    (1, 2, 1, 64, 3, 1),      # one query row and one key per block
 ]
 
 
