@@ -48,17 +48,8 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 }
 
 // One 64-row block per work-group (256 threads, 16-byte chunks of 8 values).
-// With ROT (incoherent processing), each row is first multiplied by diag(signs) H_D, H_D
-// the Sylvester Hadamard matrix (entries +-1), in fp32 by the fast transform: for
-// h = 1, 2, 4, ..., D/2 every pair of entries (i, i + h) with i & h == 0 becomes
-// (a + b, a - b).  A row's D values sit in D/8 consecutive lanes, 8 per lane, so the
-// stages h < 8 run inside a lane and the others pair lane L with lane L ^ (h / 8); each
-// entry goes through the same fp32 operations in the same order whichever lane computes
-// it.  The block is then quantized as without ROT, and its descale multiplied by `post`
-// (1, or 1/D for the query side: a power of two, exact).
-template <int D, bool ROT>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, const float *signs,
-                                                         float post, uint8_t *codes,
+template <int D>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, uint8_t *codes,
                                                          float *descale, int32_t n_seg,
                                                          int64_t seg, int32_t T) {
     constexpr int CPR = D / 8;               // chunks per row
@@ -74,46 +65,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, const fl
     const int64_t left = seg - (int64_t)u * QT;
     const int nrows = left < QT ? (int)left : QT;
     const int64_t base = (hd * n_seg * seg + row0) * D;  // element offset of the block
-    const int c = threadIdx.x % CPR;                    // this thread's chunk of each row
 
     float f[PER][8];
-    float sg[8];
-    if constexpr (ROT) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sg[e] = signs[8 * c + e];
-    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int q = threadIdx.x + 256 * i;
         if (q / CPR < nrows) {
             const bf16x8 v = *(const bf16x8 *)(x + base + (int64_t)q * 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[i][e] = ROT ? (float)v[e] * sg[e] : (float)v[e];
+            for (int e = 0; e < 8; ++e) f[i][e] = (float)v[e];
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) f[i][e] = 0.f;
-        }
-    }
-    if constexpr (ROT) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-#pragma unroll
-            for (int h = 1; h < 8; h *= 2)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (!(e & h)) {
-                        const float a = f[i][e], b = f[i][e + h];
-                        f[i][e] = a + b;
-                        f[i][e + h] = a - b;
-                    }
-#pragma unroll
-            for (int k = 1; k < CPR; k *= 2)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float mine = f[i][e];
-                    const float other = __shfl_xor(mine, k);
-                    f[i][e] = (c & k) ? other - mine : mine + other;
-                }
         }
     }
     float amax = 0.f;
@@ -135,7 +98,91 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, const fl
                 u32x2{pack4(g[0], g[1], g[2], g[3]), pack4(g[4], g[5], g[6], g[7])};
         }
     }
-    if (threadIdx.x == 0) descale[hs * T + u] = ROT ? ds * post : ds;
+    if (threadIdx.x == 0) descale[hs * T + u] = ds;
+}
+
+// Butterfly stage across the lanes of a DPP quad: lanes L and L ^ K hold entries i and
+// i + K * D / 4 of one row; the lower lane becomes a + b, the upper a - b, each computed as
+// partner + (+-own), one fp32 rounding either way as in a + b and a - b.  The partner's
+// value comes by a DPP quad permute ([1, 0, 3, 2] for K = 1, [2, 3, 0, 1] for K = 2).
+template <int K, int N>
+__device__ __forceinline__ void quad_stage(float (&f)[N], int qd) {
+    static_assert(K == 1 || K == 2, "lanes of one quad");
+    const unsigned flip = (qd & K) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        const int mine = __builtin_bit_cast(int, f[e]);
+        const int other = __builtin_amdgcn_mov_dpp(mine, K == 1 ? 0xB1 : 0x4E, 0xF, 0xF, true);
+        f[e] = __builtin_bit_cast(float, other) + __builtin_bit_cast(float, (unsigned)mine ^ flip);
+    }
+}
+
+// Rows mode with incoherent processing: each row is first multiplied by diag(signs) H_D,
+// H_D the Sylvester Hadamard matrix (entries +-1), in fp32 by the fast transform: for
+// h = 1, 2, 4, ..., D/2 every pair of entries (i, i + h) with i & h == 0 becomes
+// (a + b, a - b).  One 64-row block per work-group; a row's D values sit in the four lanes
+// of a DPP quad, D/4 consecutive values per lane, so the stages h < D/4 run inside the lane
+// and the last two pair lane L with L ^ 1, then L ^ 2.  Every entry goes through the same
+// fp32 operations in the same order whichever lane computes it.  The block is then
+// quantized as in rows mode, and its descale multiplied by `post` (1, or 1/D for the query
+// side: a power of two, exact).
+template <int D>
+__global__ __launch_bounds__(256) void quant_rows_rot_kernel(const bf16 *x, const float *signs,
+                                                             float post, uint8_t *codes,
+                                                             float *descale, int32_t n_seg,
+                                                             int64_t seg, int32_t T) {
+    constexpr int VPL = D / 4;  // values per lane: 32 (d = 128) or 16 (d = 64)
+    __shared__ float red[4];
+    const int64_t wg = blockIdx.x;
+    const int u = (int)(wg % T);
+    const int64_t hs = wg / T;  // head * n_seg + segment
+    const int s = (int)(hs % n_seg);
+    const int64_t hd = hs / n_seg;
+    const int64_t row0 = (int64_t)s * seg + (int64_t)u * QT;
+    const int64_t left = seg - (int64_t)u * QT;
+    const int nrows = left < QT ? (int)left : QT;
+    const int r = threadIdx.x >> 2, qd = threadIdx.x & 3;  // row of the block, quarter of it
+    const int64_t off = (hd * n_seg * seg + row0 + r) * D + qd * VPL;  // this lane's values
+    float f[VPL];
+    if (r < nrows) {
+#pragma unroll
+        for (int k = 0; k < VPL / 8; ++k) {
+            const bf16x8 v = *(const bf16x8 *)(x + off + 8 * k);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[8 * k + e] = (float)v[e] * signs[qd * VPL + 8 * k + e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) f[e] = 0.f;
+    }
+#pragma unroll
+    for (int h = 1; h < VPL; h *= 2)
+#pragma unroll
+        for (int e = 0; e < VPL; ++e)
+            if (!(e & h)) {
+                const float a = f[e], b = f[e + h];
+                f[e] = a + b;
+                f[e + h] = a - b;
+            }
+    quad_stage<1>(f, qd);
+    quad_stage<2>(f, qd);
+    float amax = 0.f;  // rows past the block's end hold zeros
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) amax = fmaxf(amax, fabsf(f[e]));
+    const float ds = descale_of(block_max(amax, red));
+    const float inv = 1.0f / ds;
+    if (r < nrows) {
+#pragma unroll
+        for (int k = 0; k < VPL / 16; ++k) {
+            const float *g = f + 16 * k;
+            *(u32x4 *)(codes + off + 16 * k) =
+                u32x4{pack4(g[0] * inv, g[1] * inv, g[2] * inv, g[3] * inv),
+                      pack4(g[4] * inv, g[5] * inv, g[6] * inv, g[7] * inv),
+                      pack4(g[8] * inv, g[9] * inv, g[10] * inv, g[11] * inv),
+                      pack4(g[12] * inv, g[13] * inv, g[14] * inv, g[15] * inv)};
+        }
+    }
+    if (threadIdx.x == 0) descale[hs * T + u] = ds * post;
 }
 
 __global__ void fill_zero_kernel(float *p, int64_t n) {
@@ -247,8 +294,12 @@ hipError_t rows_impl(const void *x, const float *signs, float post, uint8_t *cod
                      hipStream_t st) {
     const int32_t T = (int32_t)((seg + QT - 1) / QT);
     const int64_t n = heads * n_seg * T;
-    hipLaunchKernelGGL((quant_rows_kernel<D, ROT>), dim3((unsigned)n), dim3(256), 0, st,
-                       (const bf16 *)x, signs, post, codes, descale, n_seg, seg, T);
+    if constexpr (ROT)
+        hipLaunchKernelGGL((quant_rows_rot_kernel<D>), dim3((unsigned)n), dim3(256), 0, st,
+                           (const bf16 *)x, signs, post, codes, descale, n_seg, seg, T);
+    else
+        hipLaunchKernelGGL((quant_rows_kernel<D>), dim3((unsigned)n), dim3(256), 0, st,
+                           (const bf16 *)x, codes, descale, n_seg, seg, T);
     return hipGetLastError();
 }
 
