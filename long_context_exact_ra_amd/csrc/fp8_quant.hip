@@ -66,19 +66,21 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16 *x, uint8_t 
     const int nrows = left < QT ? (int)left : QT;
     const int64_t base = (hd * n_seg * seg + row0) * D;  // element offset of the block
 
-    float f[PER][8];
+    // Loads without branches (chunks of rows past the block's end read the last row's chunk,
+    // then count as zeros), so a thread's loads are in flight together.
+    bf16x8 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int q = threadIdx.x + 256 * i;
-        if (q / CPR < nrows) {
-            const bf16x8 v = *(const bf16x8 *)(x + base + (int64_t)q * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[i][e] = (float)v[e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[i][e] = 0.f;
-        }
+        const int qq = q / CPR < nrows ? q : (nrows - 1) * CPR + q % CPR;
+        v[i] = *(const bf16x8 *)(x + base + (int64_t)qq * 8);
     }
+    float f[PER][8];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            f[i][e] = (threadIdx.x + 256 * i) / CPR < nrows ? (float)v[i][e] : 0.f;
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
@@ -202,9 +204,12 @@ __global__ __launch_bounds__(256) void vt_amax_kernel(const bf16 *x, float *amax
     const int64_t r0 = (int64_t)(blockIdx.x % n_chunks) * 256;
     const int c8 = threadIdx.x % CPR, rp = threadIdx.x / CPR;
     float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r = rp; r < 256; r += RPP) {
-        const int64_t row = r0 + r;
-        if (row >= rows) break;
+    // A fixed trip count without branches, so all of a thread's loads can be in flight at
+    // once: rows past the head's end read its last row again, which leaves a maximum as is.
+#pragma unroll
+    for (int k = 0; k < 256 / RPP; ++k) {
+        const int64_t want = r0 + rp + k * RPP;
+        const int64_t row = want < rows ? want : rows - 1;
         const bf16x8 v = *(const bf16x8 *)(x + (hd * rows + row) * D + 8 * c8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf((float)v[e]));
@@ -255,19 +260,19 @@ __global__ __launch_bounds__(256) void vt_quant_kernel(const bf16 *x, uint8_t *c
     float inv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) inv[e] = 1.0f / descale[hd * D + 8 * c8 + e];
-    float f[RPT][8];
+    // Loads without branches (rows past the segment's end read its last row, then count as
+    // zeros), so a thread's loads are in flight together.
+    bf16x8 v[RPT];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-        const int r = r0 + k;
-        if (r < nrows) {
-            const bf16x8 v = *(const bf16x8 *)(xt + (int64_t)r * D + 8 * c8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[k][e] = (float)v[e] * inv[e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[k][e] = 0.f;
-        }
+        const int r = r0 + k < nrows ? r0 + k : nrows - 1;
+        v[k] = *(const bf16x8 *)(xt + (int64_t)r * D + 8 * c8);
     }
+    float f[RPT][8];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[k][e] = r0 + k < nrows ? (float)v[k][e] * inv[e] : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         uint8_t *tp = tile + (8 * c8 + e) * VS + r0;
