@@ -126,6 +126,12 @@ def _dev(t: torch.Tensor | None, name: str):
         return None
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a tensor in GPU memory")
+    # The library launches on the current device: memory of another GPU is refused here
+    # rather than handed to a kernel that cannot address it.
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"{name} is on {t.device}, but calls run on the current device "
+                         f"cuda:{cur} (select it with torch.cuda.device)")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -141,6 +147,9 @@ def _need_shape(t: torch.Tensor, shape, name: str, dtype=None, contiguous=True):
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
+    elif stream.device.index != torch.cuda.current_device():
+        raise ValueError(f"the stream belongs to {stream.device}, but calls run on the "
+                         f"current device cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
