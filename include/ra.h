@@ -14,7 +14,8 @@
  * over K/V blocks that are already resident in device memory.
  *
  * Conventions for every entry point
- *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *  - All tensor pointers are DEVICE pointers owned by the caller, in memory of the
+ *    current HIP device (hipSetDevice), on which every call launches; the library
  *    allocates no device memory and keeps no state between calls, except a
  *    per-device record of whether the device is supported.
  *  - Layouts are row-major: Q_i and outputs O are [B, H, l_q, d]; K and V are
