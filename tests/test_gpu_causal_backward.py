@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from long_context_exact_ra_amd import ra, synth
-from test_gpu_backward import TOL, _bits, _draw, check, sampled_magnitudes
+from test_gpu_backward import TOL, _bits, _draw, _tile_edge_rows, check, sampled_magnitudes
 from test_gpu_parity import _say
 
 pytestmark = pytest.mark.gpu
@@ -165,5 +165,41 @@ def test_32k_share_sampled_rows(dev, layout):
                                     ("dV", dV[b, h, k_rows], rv, mv)):
             w_ = check(f"32K {layout} head {h} {name}", got, ref, mag)
             _say(f"[causal backward 32K {layout}] head {h} {name}: err/bound {w_:.3f}")
+            zero = np.all(ref == 0, axis=1)
+            assert np.all(got[zero] == 0), f"head {h} {name}: unseen rows not zero"
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_128k_share_sampled_rows(dev, layout):
+    """The 128K / N = 8 causal share the benchmark reports (H = 32, d = 128, rank 3) at full
+    size: dQ on query rows at both sides of 256-row tile edges and the ends, dK / dV on key
+    rows at both sides of 128-row tile edges, the ends and the edges of the member's own
+    block, one head, elementwise within TOL * mag; rows no query of the share sees are
+    exactly zero."""
+    w = synth.WORKLOADS["share_L128K_N8"]
+    q, k, v = synth.draw_workload(w)
+    g = torch.Generator().manual_seed(w.seed + 99)
+    do = torch.randn((w.B, w.H, w.l, w.d), generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(w.d)
+    _say(f"[causal backward 128K {layout}] running forward + backward")
+    dQ, dK, dV = run_gpu(q, k, v, do, w.N, w.rank, layout, scale, dev)
+    heads = [(0, 1)]
+    q_rows = _tile_edge_rows(w.l, 256)
+    lq = w.l
+    k_rows = sorted(set(_tile_edge_rows(w.L, 128)) |
+                    {w.rank * lq - 1, w.rank * lq, w.rank * lq + lq - 1, (w.rank + 1) * lq})
+    _say(f"[causal backward 128K {layout}] oracle and magnitudes on {len(q_rows)} query and "
+         f"{len(k_rows)} key rows")
+    bits = [_bits(x) for x in (q, k, v, do)]
+    res = oracle.share_backward_rows(*bits, scale, heads, q_rows, k_rows, rank=w.rank, N=w.N,
+                                     layout=layout)
+    mags = sampled_magnitudes(q, k, v, do, scale, heads, q_rows, k_rows, rank=w.rank, N=w.N,
+                              layout=layout)
+    for (b, h), (rq, rk, rv), (mq, mk, mv) in zip(heads, res, mags):
+        for name, got, ref, mag in (("dQ", dQ[b, h, q_rows], rq, mq),
+                                    ("dK", dK[b, h, k_rows], rk, mk),
+                                    ("dV", dV[b, h, k_rows], rv, mv)):
+            w_ = check(f"128K {layout} head {h} {name}", got, ref, mag)
+            _say(f"[causal backward 128K {layout}] head {h} {name}: err/bound {w_:.3f}")
             zero = np.all(ref == 0, axis=1)
             assert np.all(got[zero] == 0), f"head {h} {name}: unseen rows not zero"
