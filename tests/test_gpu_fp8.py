@@ -297,3 +297,26 @@ def test_fp8_causal_32k_sampled_rows(dev, layout):
     compare_rows(O, m, lo, Oc, ref, scale, w.rank, w.N, local, f"causal 32K {layout}",
                  out_rows=h * w.l + local, layout=layout)
 
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_fp8_causal_128k_sampled_rows(dev, layout):
+    """The 128K / N = 8 causal share the benchmark reports, from E4M3 inputs quantized on the
+    GPU, every layout: for one head the oracle quantizes the same bf16 inputs (codes compared
+    bit for bit) and evaluates rows at the ends and both sides of the first and last 256-row
+    work-group edge and of every 1024-row edge, within the FP8 bound over admissible keys."""
+    w = synth.WORKLOADS["share_L128K_N8"]
+    q, k, v = synth.draw_workload(w)
+    scale = 1.0 / math.sqrt(w.d)
+    _say(f"[fp8 causal 128K {layout}] quantizing and running the share on the GPU")
+    (O, m, lo, Oc), gpu = run_fp8_share(q, k, v, w.N, w.rank, scale, dev, cast=True,
+                                        layout=layout)
+    Q8, qs, K8, ks, V8, vs = gpu
+    local = set(synth.boundary_rows(1, 1, w.l, 0, w.seed, tile=1024))
+    local = np.array(sorted(local | {255, 256, w.l - 257, w.l - 256}), np.int64)
+    h = 1
+    ref = oracle_codes(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], w.N)
+    assert_codes_equal((Q8[:, h:h + 1], qs[:, h:h + 1], K8[:, h:h + 1], ks[:, h:h + 1],
+                        V8[:, h:h + 1], vs[:, h:h + 1]), ref, f"128K {layout}")
+    compare_rows(O, m, lo, Oc, ref, scale, w.rank, w.N, local, f"causal 128K {layout}",
+                 out_rows=h * w.l + local, layout=layout)
+
