@@ -359,6 +359,48 @@ def test_full_size_workload_sampled_rows(dev, name):
          f"{worst[1]:.3f}, lse err/bound {worst[2]:.3f}")
 
 
+def test_full_size_step_path_sampled_rows(dev):
+    """The per-step path the benchmark also times on the 128K share (N ra_step calls over
+    views of the resident K/V in ring order, then ra_finalize), at full size, against the
+    oracle on every head's first and last row and both sides of every 256-row query-tile
+    boundary (4096 rows)."""
+    w = synth.WORKLOADS["share_L128K_N8"]
+    _say("[step path 128K] drawing inputs")
+    q, k, v = synth.draw_workload(w)
+    scale = 1.0 / math.sqrt(w.d)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    O_acc = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.float32, device=dev)
+    m = torch.empty((w.B, w.H, w.l), dtype=torch.float32, device=dev)
+    lsum = torch.empty_like(m)
+    _say(f"[step path 128K] {w.N} steps of rank {w.rank}, then finalize")
+    ra.state_init(O_acc, m, lsum)
+    for j in ra.ring_schedule(w.rank, w.N):
+        ra.step(qd, kd[:, :, j * w.l:(j + 1) * w.l], vd[:, :, j * w.l:(j + 1) * w.l], O_acc, m,
+                lsum, scale)
+    cast = torch.empty((w.B, w.H, w.l, w.d), dtype=torch.bfloat16, device=dev)
+    ra.finalize(O_acc, lsum, O_out=cast)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O_acc).all()
+    assert torch.equal(cast, O_acc.to(torch.bfloat16))
+    rows = synth.boundary_rows(w.B, w.H, w.l, 0, w.seed)
+    Q, K, V = host(q, k, v)
+    Og = flat_rows(O_acc, rows).cpu().numpy()
+    mg, lg = flat_rows(m, rows).cpu().numpy(), flat_rows(lsum, rows).cpu().numpy()
+    worst = [0.0, 0.0, 0.0]
+    for i0 in range(0, len(rows), 1024):
+        part = rows[i0:i0 + 1024]
+        _say(f"[step path 128K] oracle on rows {i0}..{i0 + len(part) - 1} of {len(rows)}")
+        Or, M, Z = oracle.share(Q, K, V, scale, w.rank, w.N, rows=part)
+        sl = slice(i0, i0 + len(part))
+        err = check_O(Og[sl], Or, "bf16", "step path 128K")
+        bnd = stat_bounds_bf16(Q, K, (w.B, w.H, w.H_kv, w.d, w.l, w.L), scale, part, M,
+                               n_tiles=w.N * -(-w.l // 64), n_steps=w.N)
+        wm, wl = check_stats(mg[sl], lg[sl], M, Z, "bf16", "step path 128K", bounds=bnd)
+        worst = [max(worst[0], err), max(worst[1], wm), max(worst[2], wl)]
+    _say(f"[step path 128K] {len(rows)} rows: max abs err {worst[0]:.2e}, m err/bound "
+         f"{worst[1]:.3f}, lse err/bound {worst[2]:.3f}")
+
+
 def test_largest_head_range(dev):
     """The largest key range one head may span: 2^23 - 1 keys of d = 128 bf16 are 2^31 - 256
     bytes, the edge of the kernel's 32-bit buffer range (one key more is RA_ENOTSUP, checked
